@@ -1,0 +1,142 @@
+"""The five workloads of the local-expert MoE block.
+
+Shapes follow the Muse Spark K3 page (module docstring: one rank of a TP = EP = 8
+group owns experts [32 r, 32 r + 32) of 256, top-8 routing) and the K5 page
+(HA routing tail: 32 experts a rank, top-8; row sets S = 32..128). Token rows are
+spec-verify rows, all valid.
+
+Routing structure is imposed only through the router bias (``bias_kind``):
+
+* ``none``    -- no bias: every expert equally likely.
+* ``local``   -- bias ``beta`` on the local experts [local_base, local_base + n_local)
+                 so that about a quarter of all picks land on them.
+* ``zipf``    -- expert popularity shaped as Zipf(s) through a bias
+                 ``-s * ln(rank_e)``, with the ranks interleaved so that the local
+                 experts sample the whole popularity curve (rank 8 j + 3 for local
+                 expert j) instead of holding only its head.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+
+@dataclasses.dataclass(frozen=True)
+class MoeConfig:
+    name: str
+    S: int  # token rows
+    d: int  # hidden size seen by the experts
+    E: int  # experts routed over
+    topk: int  # picks per token
+    n_local: int  # experts held by this GPU
+    local_base: int  # first local expert id
+    I: int  # expert intermediate size  # noqa: E741
+    shared_I: int = 0  # 0: no shared expert
+    renorm: int = 1  # routing weights renormalised over the top-k
+    eps: float = 1e-6  # post-expert RMSNorm epsilon
+    bias_kind: str = "none"
+    beta: float = 0.0  # "local" bias value
+    zipf_s: float = 0.0  # "zipf" exponent
+    x_std: float = 1.0
+    wr_std: float = 0.02
+    ws_std: float = 0.02  # shared-expert weights
+    e8m0_lo: int = 119  # e8m0 scale bytes drawn uniformly from [lo, hi]
+    e8m0_hi: int = 127
+    desc: str = ""
+
+    def dims(self) -> dict:
+        return dict(
+            S=self.S,
+            d=self.d,
+            E=self.E,
+            topk=self.topk,
+            n_local=self.n_local,
+            local_base=self.local_base,
+            I=self.I,
+            renorm=self.renorm,
+            eps=self.eps,
+            shared_I=self.shared_I,
+        )
+
+    def with_(self, **kw) -> "MoeConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# "local" bias: beta = 0.50 gives 25.1 % local picks with this generator at
+# d = 4096, router std 0.02 (mean over seeds 0..63 of 16 tokens x 8 picks; the
+# per-seed spread is +- 3.7 %; 0.48 gives 24.4 %, 0.52 gives 25.9 %).
+_BETA_25 = 0.50
+
+CONFIGS = {
+    "tiny": MoeConfig(
+        name="tiny",
+        S=8,
+        d=256,
+        E=8,
+        topk=2,
+        n_local=8,
+        local_base=0,
+        I=128,
+        desc="S=8, d=256, 8 experts all local, I=128, top-2",
+    ),
+    "s8_uniform": MoeConfig(
+        name="s8_uniform",
+        S=8,
+        d=4096,
+        E=256,
+        topk=8,
+        n_local=32,
+        local_base=0,
+        I=2048,
+        desc="S=8, d=4096, 256 experts (32 local), I=2048, top-8, uniform routing",
+    ),
+    "s16_local25": MoeConfig(
+        name="s16_local25",
+        S=16,
+        d=4096,
+        E=256,
+        topk=8,
+        n_local=32,
+        local_base=0,
+        I=2048,
+        bias_kind="local",
+        beta=_BETA_25,
+        desc="S=16, as s8_uniform, router bias so ~25% of picks are local",
+    ),
+    "s64_zipf": MoeConfig(
+        name="s64_zipf",
+        S=64,
+        d=4096,
+        E=256,
+        topk=8,
+        n_local=32,
+        local_base=0,
+        I=2048,
+        bias_kind="zipf",
+        zipf_s=1.1,
+        desc="S=64, as s8_uniform, Zipf(1.1) expert popularity via router bias",
+    ),
+    "s128_shared": MoeConfig(
+        name="s128_shared",
+        S=128,
+        d=7168,
+        E=256,
+        topk=8,
+        n_local=32,
+        local_base=0,
+        I=2048,
+        shared_I=2048,
+        desc="S=128, d=7168, 256 experts (32 local), I=2048, top-8, uniform, "
+        "+ dense bf16 shared expert (I_s=2048)",
+    ),
+}
+
+# the order the workloads are listed in: tiny first, then S = 8, 16, 64, 128
+CONFIG_ORDER = ["tiny", "s8_uniform", "s16_local25", "s64_zipf", "s128_shared"]
+
+
+def get_config(name: str) -> MoeConfig:
+    try:
+        return CONFIGS[name]
+    except KeyError:
+        raise KeyError(f"unknown workload {name!r}; known: {CONFIG_ORDER}") from None
