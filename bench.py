@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the local-expert MoE block on one MI355X.
+
+A step is one pass of the whole block -- moe_route -> moe_bucket ->
+moe_expert_ffn -> moe_combine -- over one batch of S token rows, all inputs
+resident in HBM. The default workload is S = 8, d = 4096, 256 experts (32
+local), I = 2048, top-8 uniform routing ("s8_uniform").
+
+Last-level-cache control: MI355X's 256 MB Infinity Cache would hold one
+step's active weights (about 94 MB here), so the benchmark keeps R copies of
+every weight set with R x (active bytes) >= 512 MiB and rotates through them
+step by step; every step then streams its weights from HBM, as a decode step
+does between the other layers' weights.
+
+Output: one JSON line (see the fields below). ``roofline`` covers the
+dominant call, moe_expert_ffn, timed with HIP events on its stream in a second
+timed pass; its ``traffic`` comes from the committed rocprofv3 counter summary
+when that summary was taken on the current FFN source, else null.
+``cpu_baseline`` times the CPU oracle on the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+LLC_BYTES = 256 * 2**20  # MI355X Infinity Cache
+FFN_SOURCES = ["moe_decode_layer_router_amd/csrc/ffn.hip", "moe_decode_layer_router_amd/csrc/common.h"]
+
+
+def ffn_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in FFN_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes a moe_expert_ffn call moves, from profiles/, if taken on the
+    current FFN source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"expert_ffn_{workload}_traffic.md")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m_sha = re.search(r"ffn_source_sha:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != ffn_source_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def expert_bytes(cfg) -> int:
+    """MXFP4 bytes of one expert: gate_up + down, values + e8m0 scales."""
+    return 3 * cfg.I * cfg.d * 17 // 32
+
+
+def cpu_baseline(inp, budget_s: float) -> dict:
+    """The CPU oracle (single thread, as it stands) on whole steps of the same
+    workload until about budget_s seconds have passed (at least one step)."""
+    import oracle
+
+    cfg = inp["cfg"]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(inp)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / n * (n + 1) > 2.5 * budget_s:
+            break
+    return {
+        "value": round(cfg.S * n / el, 3),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n} whole steps of {cfg.name} (S={cfg.S}) on the same inputs, single thread, "
+        f"{el:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="s8_uniform")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(
+            f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU's share of the "
+            "expert-parallel block (no collectives); run with --gpus 1",
+            file=sys.stderr,
+        )
+        return 2
+
+    import torch
+
+    from moe_decode_layer_router_amd.block import MoeBlock
+    from synth import get_config, make_inputs
+
+    cfg = get_config(args.workload)
+    inp = make_inputs(cfg, 0)
+    torch.cuda.set_device(0)
+    blk = MoeBlock(inp, device="cuda:0")
+    blk.step(0)
+    torch.cuda.synchronize()
+    counts = blk.counts.cpu().numpy()
+    n_active = int((counts > 0).sum())
+    picks = int(counts.sum())
+    b_mx = n_active * expert_bytes(cfg)
+    b_router = cfg.E * cfg.d * 4
+    b_shared = 3 * cfg.shared_I * cfg.d * 2
+    b_step_w = b_mx + b_router + b_shared
+    copies = args.copies or max(1, math.ceil(2 * LLC_BYTES / max(b_step_w, 1)))
+    blk.add_weight_copies(copies - 1)
+    torch.cuda.synchronize()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * 2**20 // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for i in range(args.warmup):
+        blk.step(i % copies)
+    torch.cuda.synchronize()
+
+    # timed pass 1: whole steps
+    K = args.steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K):
+        blk.step(i % copies)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+
+    # timed pass 2: the expert FFN call alone, events on its stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        s = i % copies
+        blk.route(s)
+        blk.bucket()
+        evs[i][0].record()
+        blk.expert_ffn(s)
+        evs[i][1].record()
+        blk.combine()
+    torch.cuda.synchronize()
+    ffn_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+
+    R = blk.dims.r_max
+    # algorithmic bytes of one moe_expert_ffn call: the active experts' MXFP4
+    # weights, the shared expert's bf16 weights, x read, h written and read,
+    # y written
+    b_act = cfg.S * cfg.d * 2 + picks * cfg.I * 2 * 2 + picks * cfg.d * 2
+    if cfg.shared_I:
+        b_act += cfg.S * cfg.shared_I * 2 * 2 + cfg.S * cfg.d * 2
+    ffn_bytes = b_mx + b_shared + b_act
+    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    traffic = committed_traffic(cfg.name)
+
+    tok_s = cfg.S / (ms * 1e-3)
+    line = {
+        "metric": "tokens/s and MXFP4 weight HBM GB/s (% of peak), local-expert MoE, S=8..128",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 weights -> bf16 MFMA, fp32 accumulation",
+        "data": "synthetic (seeded generator, seed 0)",
+        "config": {
+            "workload": cfg.name,
+            "S": cfg.S,
+            "d": cfg.d,
+            "E": cfg.E,
+            "n_local": cfg.n_local,
+            "I": cfg.I,
+            "topk": cfg.topk,
+            "shared_I": cfg.shared_I,
+            "active_local_experts": n_active,
+            "local_picks": picks,
+            "weight_copies_rotated": copies,
+        },
+        "mxfp4_weight_gbps": round(b_mx / (ms * 1e-3) / 1e9, 1),
+        "all_weight_pct_hbm_peak": round(100 * b_step_w / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "kernel": "moe_expert_ffn (gate_up + down launches"
+            + (", shared expert launches" if cfg.shared_I else "")
+            + ")",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": ffn_bytes,
+            "avg_ms": round(ffn_ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

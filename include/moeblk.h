@@ -1,0 +1,197 @@
+/*
+ * moeblk.h -- C ABI of the local-expert MoE block for AMD MI355X (gfx950).
+ *
+ * One GPU's share of an expert-parallel MoE layer in a spec-verify decode step:
+ * S token rows (1..128, all valid) are routed over E experts with sigmoid
+ * top-k; the picks that land on this GPU's n_local experts run through MXFP4
+ * gate_up -> SwiGLU -> MXFP4 down, each expert output is RMS-normalised, and
+ * the routing-weighted sum is written as this GPU's fp32 partial.
+ *
+ * Sources (vLLM API pages):
+ *   - Muse Spark K3 page (vllm.models.muse_spark.amd.mono.kernels.k3), module
+ *     docstring, stages "A" (fp32 router logits), "route" (every token's top-8,
+ *     the local experts' picks), "C, D" (MXFP4 gate_up / down decoded in
+ *     registers, bf16 MFMA), "E" (per-pick post-expert norm and weighted sum
+ *     into the expert-parallel partial); functions "mx_chunk", "fp4_mma",
+ *     "dn_loads" (MXFP4 rows in 256-K chunks with e8m0 scales; the
+ *     active-expert table).
+ *   - Muse Spark K5 page (vllm.models.muse_spark.amd.mono.kernels.k5), module
+ *     docstring: the HA routing tail hands top-k ids and weights to HM, the
+ *     local-expert launch; every row tile is 16 tokens.
+ *   - Kimi-K3 layer page (...specialized_decode.mono.layer), "k2_launch": router
+ *     weight plus bias, MoE weights as separate value / scale tensors, shared
+ *     expert gate_up / down weights, caller-provided scratch.
+ *
+ * Conventions (every entry point):
+ *   - All pointers are device pointers unless stated otherwise, caller-owned,
+ *     16-byte aligned, tensors contiguous row-major. The library never
+ *     allocates or frees memory and never synchronises: work is enqueued on
+ *     `stream` (NULL = the null stream) and the call returns.
+ *   - bf16 tensors are passed as `const void*` (16-bit bf16 bit patterns).
+ *   - Return value: MOE_OK, or a negative MOE_ERR_* code. Every argument check
+ *     runs on the host before anything is enqueued, so a rejected call has no
+ *     effect. MOE_ERR_HIP reports a failed launch (hipGetLastError).
+ *   - Device data (ids, counts, ...) are trusted: they are not range-checked
+ *     on the device beyond what each function states.
+ *   - Calls on one stream run in order; the block is
+ *       moe_route -> moe_bucket -> moe_expert_ffn -> moe_combine.
+ */
+#ifndef MOEBLK_H
+#define MOEBLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEBLK_ABI_VERSION 1
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)       /* a size is out of range or inconsistent */
+#define MOE_ERR_ALIGN (-3)       /* a pointer is not 16-byte aligned */
+#define MOE_ERR_UNSUPPORTED (-4) /* a valid but unsupported parameter (which, renorm, ...) */
+#define MOE_ERR_WORKSPACE (-5)   /* workspace smaller than moe_ffn_workspace_bytes() */
+#define MOE_ERR_HIP (-6)         /* the HIP runtime reported an error */
+
+/* weight selectors for the packing calls */
+#define MOE_W13 0 /* gate_up: N = 2 I rows (rows [0, I) gate, [I, 2 I) up), K = d */
+#define MOE_W2 1  /* down:    N = d rows, K = I */
+
+/* Problem sizes, all in elements. Supported ranges:
+ *   1 <= S <= 128; 128 <= d <= 16384, d % 128 == 0; 1 <= E <= 256;
+ *   1 <= topk <= 8, topk <= E; 1 <= n_local <= 32;
+ *   0 <= local_base, local_base + n_local <= E;
+ *   128 <= I <= 8192, I % 128 == 0; renorm in {0, 1}; eps finite, >= 0;
+ *   shared_I == 0 or (128 <= shared_I <= 8192, shared_I % 128 == 0). */
+typedef struct moe_dims {
+  int32_t S;          /* token rows */
+  int32_t d;          /* hidden size seen by the experts */
+  int32_t E;          /* experts routed over (router rows) */
+  int32_t topk;       /* picks per token */
+  int32_t n_local;    /* experts held by this GPU */
+  int32_t local_base; /* id of the first local expert; local ids are [local_base, local_base + n_local) */
+  int32_t I;          /* expert intermediate size */
+  int32_t renorm;     /* 1: w = sigmoid / sum of the token's topk sigmoids; 0: w = sigmoid */
+  float eps;          /* post-expert RMSNorm epsilon */
+  int32_t shared_I;   /* 0: no shared expert; else its intermediate size */
+} moe_dims;
+
+/* R_max = S * min(topk, n_local): the most local picks a call can have
+ * (a token's picks are distinct experts). Bucket rows, h rows and routed y
+ * rows are indexed 0 .. R_max - 1. */
+
+int moe_abi_version(void);
+
+/* A static English description of a status code. Never NULL. */
+const char* moe_status_string(int status);
+
+/* Host-only check of `dims` against the supported ranges: MOE_OK,
+ * MOE_ERR_NULL, MOE_ERR_SHAPE or MOE_ERR_UNSUPPORTED. */
+int moe_check_dims(const moe_dims* dims);
+
+/* ------------------------------------------------------------------------ */
+/* one-time weight packing (not part of the per-step path)                   */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of the packed MXFP4 weight `which` (MOE_W13 / MOE_W2) of all n_local
+ * experts, or 0 if `dims` is invalid. Equals n_local * N * K * (1/2 + 1/32). */
+size_t moe_packed_mxfp4_bytes(const moe_dims* dims, int which);
+
+/* Repack canonical MXFP4 weights into the kernel's tile order (the role the
+ * K3 page's "shuffled layouts" play: the same bytes, permuted so that each
+ * wave load reads one contiguous 1 KiB).
+ *   q      [n_local, N, K/2] uint8: two e2m1 codes a byte, element k of a row
+ *          in byte k/2, the low nibble holding the even k;
+ *   scales [n_local, N, K/32] uint8: e8m0 byte of elements 32 j .. 32 j + 31;
+ *   packed [moe_packed_mxfp4_bytes(dims, which)] bytes, written.
+ * The packed buffer is opaque: only moe_expert_ffn reads it. */
+int moe_pack_mxfp4(const moe_dims* dims, int which, const void* q, const void* scales,
+                   void* packed, hipStream_t stream);
+
+/* The same for the shared expert's dense bf16 weights (needs shared_I > 0):
+ * MOE_W13: ws13 [2 shared_I, d] (rows [0, shared_I) gate, then up);
+ * MOE_W2:  ws2 [d, shared_I]. Packed size = N * K * 2 bytes. */
+size_t moe_packed_bf16_bytes(const moe_dims* dims, int which);
+int moe_pack_bf16(const moe_dims* dims, int which, const void* w, void* packed,
+                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* the block                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Router logits and top-k (K3 page stages "A" and "route"; K5 page, HA).
+ *   x        [S, d] bf16 activations;
+ *   w_router [E, d] fp32; bias [E] fp32 or NULL (added to the logit, before
+ *            ranking and sigmoid);
+ *   logits   [S, E] fp32, written: sum_j x[t][j] w_router[e][j] (+ bias[e]),
+ *            fp32 accumulation;
+ *   topk_ids [S, topk] int32, written: the token's experts by descending
+ *            logit, equal logits to the lower id;
+ *   topk_w   [S, topk] fp32, written: sigmoid(logit), divided by the sum over
+ *            the token's topk picks when renorm = 1. */
+int moe_route(const moe_dims* dims, const void* x, const float* w_router, const float* bias,
+              float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Bucketing of the local picks (K3 page stage "route"; "dn_loads": expert
+ * table etab and count nv), deterministic, no atomics on the output.
+ *   topk_ids [S, topk] int32: a token's ids must be distinct; ids outside
+ *            [local_base, local_base + n_local) are not local;
+ *   counts   [n_local] int32, written: picks of local expert el;
+ *   offsets  [n_local + 1] int32, written: exclusive prefix sum of counts;
+ *   rows     [R_max] int32, written: token of bucket row r (rows of expert
+ *            el are offsets[el] .. offsets[el + 1] - 1, tokens ascending);
+ *            -1 from offsets[n_local] on;
+ *   pick_pos [S, topk] int32, written: bucket row of each pick, -1 if not local;
+ *   active   [1 + n_local] int32, written: active[0] = number of local
+ *            experts with a pick, then their local indices ascending, then -1. */
+int moe_bucket(const moe_dims* dims, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+               int32_t* rows, int32_t* pick_pos, int32_t* active, hipStream_t stream);
+
+/* Bytes of scratch moe_expert_ffn needs: the SwiGLU outputs of every bucket
+ * row (R_max x I bf16) and, with a shared expert, of every token
+ * (S x shared_I bf16). 0 if `dims` is invalid. */
+size_t moe_ffn_workspace_bytes(const moe_dims* dims);
+
+/* The expert FFNs (K3 page stages "C, D"): for every bucket row r of local
+ * expert el (token t = rows[r]),
+ *   gu = bf16( x[t] . W13[el]^T )                (MXFP4 decoded to bf16, fp32 accumulation)
+ *   h  = bf16( silu(gu[0:I]) * gu[I:2I] )
+ *   y[r] = bf16( h . W2[el]^T ),
+ * and, if shared_I > 0, the same chain on every token t with the dense bf16
+ * shared weights into y[R_max + t].
+ *   x          [S, d] bf16;
+ *   w13_packed, w2_packed: moe_pack_mxfp4 outputs;
+ *   counts, offsets, rows, active: moe_bucket outputs;
+ *   ws13_packed, ws2_packed: moe_pack_bf16 outputs, or NULL when shared_I == 0;
+ *   y          [R_max + (shared_I ? S : 0), d] bf16, written for rows < offsets[n_local]
+ *              and the shared rows; other rows are left as they were;
+ *   workspace  device scratch of at least moe_ffn_workspace_bytes(dims); its
+ *              contents need no initialisation and are undefined afterwards. */
+int moe_expert_ffn(const moe_dims* dims, const void* x, const void* w13_packed,
+                   const void* w2_packed, const int32_t* counts, const int32_t* offsets,
+                   const int32_t* rows, const int32_t* active, const void* ws13_packed,
+                   const void* ws2_packed, void* y, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* Per-pick RMSNorm and the routing-weighted sum (K3 page stage "E"):
+ *   out[t] = sum over t's slots s in order with pick_pos[t][s] >= 0 of
+ *              topk_w[t][s] * y[p] / sqrt(mean(y[p]^2) + eps) * gamma
+ *            (+ y[R_max + t] if shared_I > 0),  p = pick_pos[t][s];
+ *   a token with no local pick (and no shared expert) gets zeros.
+ *   y        moe_expert_ffn's output; topk_w, pick_pos as above;
+ *   gamma    [d] bf16 norm weight, or NULL for ones;
+ *   out      [S, d] fp32, overwritten (this GPU's partial). */
+int moe_combine(const moe_dims* dims, const void* y, const float* topk_w, const int32_t* pick_pos,
+                const void* gamma, float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEBLK_H */

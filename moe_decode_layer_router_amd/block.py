@@ -1,0 +1,126 @@
+"""Device buffers for one MoE block and the four-call step.
+
+``MoeBlock`` owns (through torch) the packed weights, the outputs of every call
+and the FFN workspace, and runs route -> bucket -> expert FFN -> combine on the
+current stream. It allocates only in its constructor and in
+``add_weight_copies``; the four calls allocate nothing.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (
+    MOE_W13,
+    MOE_W2,
+    MoeDims,
+    dims_from,
+    moe_bucket,
+    moe_combine,
+    moe_expert_ffn,
+    moe_ffn_workspace_bytes,
+    moe_pack_bf16,
+    moe_pack_mxfp4,
+    moe_packed_bf16_bytes,
+    moe_packed_mxfp4_bytes,
+    moe_route,
+)
+
+
+def _dev(a: np.ndarray | None, device, dtype=None):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(device)
+
+
+def bf16_tensor(bits: np.ndarray | None, device):
+    """uint16 bf16 bit patterns -> a torch.bfloat16 device tensor."""
+    if bits is None:
+        return None
+    return _dev(np.ascontiguousarray(bits).view(np.int16), device, torch.bfloat16)
+
+
+class MoeBlock:
+    """Inputs from ``synth.make_inputs`` (canonical layouts) on ``device``."""
+
+    def __init__(self, inp: dict, device="cuda", weight_copies: int = 1):
+        cfg = inp["cfg"]
+        self.cfg = cfg
+        self.dims: MoeDims = dims_from(cfg)
+        dv = torch.device(device)
+        self.device = dv
+        S, d, E, k, n = cfg.S, cfg.d, cfg.E, cfg.topk, cfg.n_local
+        R = self.dims.r_max
+        self.x = bf16_tensor(inp["x"], dv)
+        self.gamma = bf16_tensor(inp.get("gamma"), dv)
+        # weight sets (router + routed experts + shared expert); several copies
+        # let a benchmark rotate through more bytes than the last-level cache
+        self.sets = []
+        w13q = _dev(inp["w13q"], dv)
+        w13s = _dev(inp["w13s"], dv)
+        w2q = _dev(inp["w2q"], dv)
+        w2s = _dev(inp["w2s"], dv)
+        ws13 = bf16_tensor(inp.get("ws13"), dv)
+        ws2 = bf16_tensor(inp.get("ws2"), dv)
+        st = {}
+        st["wr"] = _dev(inp["wr"], dv)
+        st["bias"] = _dev(inp.get("bias"), dv)
+        st["w13"] = torch.empty(moe_packed_mxfp4_bytes(self.dims, MOE_W13), dtype=torch.uint8, device=dv)
+        st["w2"] = torch.empty(moe_packed_mxfp4_bytes(self.dims, MOE_W2), dtype=torch.uint8, device=dv)
+        moe_pack_mxfp4(self.dims, MOE_W13, w13q, w13s, st["w13"])
+        moe_pack_mxfp4(self.dims, MOE_W2, w2q, w2s, st["w2"])
+        if cfg.shared_I:
+            st["ws13"] = torch.empty(moe_packed_bf16_bytes(self.dims, MOE_W13), dtype=torch.uint8, device=dv)
+            st["ws2"] = torch.empty(moe_packed_bf16_bytes(self.dims, MOE_W2), dtype=torch.uint8, device=dv)
+            moe_pack_bf16(self.dims, MOE_W13, ws13, st["ws13"])
+            moe_pack_bf16(self.dims, MOE_W2, ws2, st["ws2"])
+        else:
+            st["ws13"] = st["ws2"] = None
+        self.sets.append(st)
+        del w13q, w13s, w2q, w2s, ws13, ws2
+        self.add_weight_copies(weight_copies - 1)
+        i32 = dict(dtype=torch.int32, device=dv)
+        self.logits = torch.empty((S, E), dtype=torch.float32, device=dv)
+        self.ids = torch.empty((S, k), **i32)
+        self.w = torch.empty((S, k), dtype=torch.float32, device=dv)
+        self.counts = torch.empty(n, **i32)
+        self.offsets = torch.empty(n + 1, **i32)
+        self.rows = torch.empty(max(R, 1), **i32)
+        self.pick_pos = torch.empty((S, k), **i32)
+        self.active = torch.empty(n + 1, **i32)
+        self.y = torch.zeros((R + (S if cfg.shared_I else 0), d), dtype=torch.bfloat16, device=dv)
+        self.out = torch.empty((S, d), dtype=torch.float32, device=dv)
+        self.ws = torch.empty(max(moe_ffn_workspace_bytes(self.dims), 16), dtype=torch.uint8, device=dv)
+
+    def add_weight_copies(self, n: int) -> None:
+        """Append n device copies of the first weight set (same bytes)."""
+        for _ in range(max(n, 0)):
+            self.sets.append({k: (None if v is None else v.clone()) for k, v in self.sets[0].items()})
+
+    # the four calls -----------------------------------------------------
+    def route(self, s=0):
+        st = self.sets[s]
+        moe_route(self.dims, self.x, st["wr"], st["bias"], self.logits, self.ids, self.w)
+
+    def bucket(self):
+        moe_bucket(self.dims, self.ids, self.counts, self.offsets, self.rows, self.pick_pos, self.active)
+
+    def expert_ffn(self, s=0):
+        st = self.sets[s]
+        moe_expert_ffn(
+            self.dims, self.x, st["w13"], st["w2"], self.counts, self.offsets, self.rows, self.active,
+            st["ws13"], st["ws2"], self.y, self.ws,
+        )
+
+    def combine(self):
+        moe_combine(self.dims, self.y, self.w, self.pick_pos, self.gamma, self.out)
+
+    def step(self, s=0):
+        self.route(s)
+        self.bucket()
+        self.expert_ffn(s)
+        self.combine()

@@ -1,0 +1,181 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+and rejects bad arguments with the documented status codes before any HIP call
+(no GPU is needed: every call below fails its host-side checks)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_decode_layer_router_amd as mb
+from synth import CONFIGS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moeblk.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced (checks fail first)
+MIS = FAKE + 4
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12, names
+    L = mb.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert mb.moe_abi_version() == 1
+    for code in range(-6, 1):
+        s = mb.moe_status_string(code)
+        assert s and s != "unknown status"
+    assert mb.moe_status_string(-99) == "unknown status"
+
+
+def dims(**kw):
+    base = dict(CONFIGS["s8_uniform"].dims())
+    base.update(kw)
+    return mb.dims_from(base)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workload_dims_are_valid(name):
+    assert mb.moe_check_dims(mb.dims_from(CONFIGS[name])) == mb.MOE_OK
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(S=0), mb.MOE_ERR_SHAPE),
+        (dict(S=129), mb.MOE_ERR_SHAPE),
+        (dict(d=4000), mb.MOE_ERR_SHAPE),
+        (dict(d=64), mb.MOE_ERR_SHAPE),
+        (dict(E=0), mb.MOE_ERR_SHAPE),
+        (dict(E=257), mb.MOE_ERR_SHAPE),
+        (dict(topk=0), mb.MOE_ERR_SHAPE),
+        (dict(topk=9), mb.MOE_ERR_SHAPE),
+        (dict(E=4, topk=5, n_local=4), mb.MOE_ERR_SHAPE),
+        (dict(n_local=0), mb.MOE_ERR_SHAPE),
+        (dict(n_local=33), mb.MOE_ERR_SHAPE),
+        (dict(local_base=-1), mb.MOE_ERR_SHAPE),
+        (dict(local_base=240), mb.MOE_ERR_SHAPE),
+        (dict(I=100), mb.MOE_ERR_SHAPE),
+        (dict(I=0), mb.MOE_ERR_SHAPE),
+        (dict(shared_I=64), mb.MOE_ERR_SHAPE),
+        (dict(renorm=2), mb.MOE_ERR_UNSUPPORTED),
+        (dict(eps=-1.0), mb.MOE_ERR_UNSUPPORTED),
+        (dict(eps=float("nan")), mb.MOE_ERR_UNSUPPORTED),
+        (dict(S=1, topk=1, n_local=1, E=1, I=128, d=128), mb.MOE_OK),
+        (dict(S=128, topk=8, E=256, local_base=224), mb.MOE_OK),
+    ],
+)
+def test_check_dims(kw, code):
+    assert mb.moe_check_dims(dims(**kw)) == code
+
+
+def test_check_dims_null():
+    assert mb.lib().moe_check_dims(None) == mb.MOE_ERR_NULL
+
+
+def test_sizes():
+    d = dims()
+    assert mb.moe_packed_mxfp4_bytes(d, mb.MOE_W13) == 32 * 4096 * 4096 * 17 // 32
+    assert mb.moe_packed_mxfp4_bytes(d, mb.MOE_W2) == 32 * 4096 * 2048 * 17 // 32
+    assert mb.moe_packed_mxfp4_bytes(d, 7) == 0
+    assert mb.moe_packed_bf16_bytes(d, mb.MOE_W13) == 0  # no shared expert
+    d4 = mb.dims_from(CONFIGS["s128_shared"])
+    assert mb.moe_packed_bf16_bytes(d4, mb.MOE_W13) == 4096 * 7168 * 2
+    assert mb.moe_packed_bf16_bytes(d4, mb.MOE_W2) == 7168 * 2048 * 2
+    R = 128 * 8
+    assert mb.moe_ffn_workspace_bytes(d4) >= R * 2048 * 2 + 128 * 2048 * 2
+    assert mb.moe_ffn_workspace_bytes(dims(S=0)) == 0
+
+
+def _rc(fn, *args):
+    return getattr(mb.lib(), fn)(*args)
+
+
+def test_route_rejects():
+    d = ctypes.byref(dims())
+    ok = [FAKE] * 6
+    assert _rc("moe_route", None, *ok, None) == mb.MOE_ERR_NULL
+    assert _rc("moe_route", ctypes.byref(dims(S=0)), *ok, None) == mb.MOE_ERR_SHAPE
+    for i in (0, 1, 3, 4, 5):  # bias (2) may be NULL
+        a = list(ok)
+        a[i] = None
+        assert _rc("moe_route", d, *a, None) == mb.MOE_ERR_NULL, i
+    for i in range(6):
+        a = list(ok)
+        a[i] = MIS
+        assert _rc("moe_route", d, *a, None) == mb.MOE_ERR_ALIGN, i
+
+
+def test_bucket_rejects():
+    d = ctypes.byref(dims())
+    ok = [FAKE] * 6
+    assert _rc("moe_bucket", ctypes.byref(dims(topk=0)), *ok, None) == mb.MOE_ERR_SHAPE
+    for i in range(6):
+        a = list(ok)
+        a[i] = None
+        assert _rc("moe_bucket", d, *a, None) == mb.MOE_ERR_NULL, i
+        a[i] = MIS
+        assert _rc("moe_bucket", d, *a, None) == mb.MOE_ERR_ALIGN, i
+
+
+def test_expert_ffn_rejects():
+    d = dims()
+    need = mb.moe_ffn_workspace_bytes(d)
+    ok = [FAKE] * 7 + [None, None] + [FAKE, FAKE]  # no shared expert: ws13/ws2 may be NULL
+    call = lambda dd, a, n=need: _rc("moe_expert_ffn", ctypes.byref(dd), *a, n, None)  # noqa: E731
+    assert call(dims(I=100), ok) == mb.MOE_ERR_SHAPE
+    for i in (0, 1, 2, 3, 4, 5, 6, 9, 10):
+        a = list(ok)
+        a[i] = None
+        assert call(d, a) == mb.MOE_ERR_NULL, i
+        a[i] = MIS
+        assert call(d, a) == mb.MOE_ERR_ALIGN, i
+    assert call(d, ok, need - 1) == mb.MOE_ERR_WORKSPACE
+    d4 = mb.dims_from(CONFIGS["s128_shared"])  # shared expert: its weights are required
+    assert call(d4, ok, mb.moe_ffn_workspace_bytes(d4)) == mb.MOE_ERR_NULL
+    a = list(ok)
+    a[7], a[8] = FAKE, MIS
+    assert call(d4, a, mb.moe_ffn_workspace_bytes(d4)) == mb.MOE_ERR_ALIGN
+
+
+def test_combine_rejects():
+    d = ctypes.byref(dims())
+    ok = [FAKE, FAKE, FAKE, None, FAKE]  # gamma may be NULL
+    assert _rc("moe_combine", None, *ok, None) == mb.MOE_ERR_NULL
+    for i in (0, 1, 2, 4):
+        a = list(ok)
+        a[i] = None
+        assert _rc("moe_combine", d, *a, None) == mb.MOE_ERR_NULL, i
+    for i in range(5):
+        a = list(ok)
+        a[i] = MIS
+        assert _rc("moe_combine", d, *a, None) == mb.MOE_ERR_ALIGN, i
+
+
+def test_pack_rejects():
+    d = ctypes.byref(dims())
+    assert _rc("moe_pack_mxfp4", d, 5, FAKE, FAKE, FAKE, None) == mb.MOE_ERR_UNSUPPORTED
+    assert _rc("moe_pack_mxfp4", d, 0, None, FAKE, FAKE, None) == mb.MOE_ERR_NULL
+    assert _rc("moe_pack_mxfp4", d, 0, MIS, FAKE, FAKE, None) == mb.MOE_ERR_ALIGN
+    assert _rc("moe_pack_bf16", d, 0, FAKE, FAKE, None) == mb.MOE_ERR_UNSUPPORTED  # no shared expert
+    d4 = ctypes.byref(mb.dims_from(CONFIGS["s128_shared"]))
+    assert _rc("moe_pack_bf16", d4, 0, None, FAKE, None) == mb.MOE_ERR_NULL
+    assert _rc("moe_pack_bf16", d4, 1, FAKE, MIS, None) == mb.MOE_ERR_ALIGN
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        mb.moe_combine(dims(), torch.zeros(4), torch.zeros(4), torch.zeros(4), None, torch.zeros(4))
