@@ -4,7 +4,9 @@
 // post-expert norm) and the picks are summed with their routing weights into
 // the expert-parallel partial, which stays fp32 (K5 page, HB: HM's partial).
 // The RMSNorm form y / sqrt(mean(y^2) + eps) * w is the one of the KDA page's
-// "kda_norm" and "stage_mix". One workgroup a token; slots in order.
+// "kda_norm" and "stage_mix". One workgroup a token; slots in order. The sum of
+// squares and the inverse root are fp64 (a bf16 row can reach 3e38, whose
+// square overflows fp32); the weighted sum is fp32.
 #include "common.h"
 #include "host.h"
 
@@ -13,13 +15,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// block-wide sum, every thread gets it; fixed order (deterministic)
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  v = wave_sum_f64(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();  // red is reused across calls
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
-  float s = red[0];
+  double s = red[0];
 #pragma unroll
   for (int i = 1; i < kThreads / kWave; ++i) s += red[i];
   return s;
@@ -31,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     const uint16_t* __restrict__ y, const float* __restrict__ tw, const int32_t* __restrict__ pick_pos,
     const uint16_t* __restrict__ gamma, float* __restrict__ out, int d, int topk, float eps,
     long shared_row0) {
-  __shared__ float red[kThreads / kWave];
+  __shared__ double red[kThreads / kWave];
   const int t = blockIdx.x;
   const int nvec = d / 8;
   float acc[VPT][8], gam[VPT][8];
@@ -53,12 +62,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
       }
     }
   }
-  const float inv_d = 1.0f / static_cast<float>(d);
+  const double inv_d = 1.0 / static_cast<double>(d);
   for (int s = 0; s < topk; ++s) {
     const int p = pick_pos[static_cast<size_t>(t) * topk + s];
     if (p < 0) continue;
     float yv[VPT][8];
-    float ss = 0.0f;
+    double ss = 0.0;  // fp64: bf16 rows reach 3e38, their squares overflow fp32
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int v = threadIdx.x + kThreads * i;
@@ -74,15 +83,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss += yv[i][j] * yv[i][j];
+      for (int j = 0; j < 8; ++j) ss += static_cast<double>(yv[i][j]) * yv[i][j];
     }
     ss = block_sum(ss, red);
-    const float r = 1.0f / sqrtf(ss * inv_d + eps);
+    const double r = 1.0 / sqrt(ss * inv_d + static_cast<double>(eps));
     const float wt = tw[static_cast<size_t>(t) * topk + s];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] += wt * (yv[i][j] * r * gam[i][j]);
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] += wt * (static_cast<float>(yv[i][j] * r) * gam[i][j]);
   }
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {

@@ -53,6 +53,10 @@ def _declare(L):
     L.orc_bucket.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
     L.orc_expert_row.argtypes = [_I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
     L.orc_shared_row.argtypes = [_I, _I, _P, _P, _P, _P, _P, _P]
+    L.orc_mx_gate_up.argtypes = [_I, _I, _P, _P, _P, _P, _P]
+    L.orc_mx_down.argtypes = [_I, _I, _P, _P, _P, _P]
+    L.orc_bf_gate_up.argtypes = [_I, _I, _P, _P, _P, _P]
+    L.orc_bf_down.argtypes = [_I, _I, _P, _P, _P]
     L.orc_expert_ffn.argtypes = [_I] * 6 + [_P] * 11
     L.orc_norm_row.argtypes = [_I, _P, _P, _D, _P]
     L.orc_combine.argtypes = [_I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P]
@@ -64,6 +68,10 @@ def _declare(L):
         "orc_bucket",
         "orc_expert_row",
         "orc_shared_row",
+        "orc_mx_gate_up",
+        "orc_mx_down",
+        "orc_bf_gate_up",
+        "orc_bf_down",
         "orc_expert_ffn",
         "orc_norm_row",
         "orc_combine",
@@ -185,6 +193,45 @@ def expert_row(x_row, w13q_e, w13s_e, w2q_e, w2s_e):
         "expert_row",
     )
     return gu, h, y
+
+
+def mx_gate_up(x_row, w13q_e, w13s_e):
+    """gate_up + SwiGLU of one row through one MXFP4 expert -> (gu, h) bf16 bits."""
+    x_row = _c(x_row, np.uint16)
+    w13q_e, w13s_e = _c(w13q_e, np.uint8), _c(w13s_e, np.uint8)
+    d = x_row.shape[0]
+    I = w13q_e.shape[0] // 2  # noqa: E741
+    gu = np.empty(2 * I, np.uint16)
+    h = np.empty(I, np.uint16)
+    _chk(lib().orc_mx_gate_up(d, I, _ptr(x_row), _ptr(w13q_e), _ptr(w13s_e), _ptr(gu), _ptr(h)), "mx_gate_up")
+    return gu, h
+
+
+def mx_down(h_row, w2q_e, w2s_e):
+    """down of one SwiGLU row through one MXFP4 expert -> y bf16 bits."""
+    h_row = _c(h_row, np.uint16)
+    w2q_e, w2s_e = _c(w2q_e, np.uint8), _c(w2s_e, np.uint8)
+    d, I = w2q_e.shape[0], h_row.shape[0]  # noqa: E741
+    y = np.empty(d, np.uint16)
+    _chk(lib().orc_mx_down(d, I, _ptr(h_row), _ptr(w2q_e), _ptr(w2s_e), _ptr(y)), "mx_down")
+    return y
+
+
+def bf_gate_up(x_row, ws13):
+    x_row, ws13 = _c(x_row, np.uint16), _c(ws13, np.uint16)
+    d, Is = x_row.shape[0], ws13.shape[0] // 2
+    gu = np.empty(2 * Is, np.uint16)
+    h = np.empty(Is, np.uint16)
+    _chk(lib().orc_bf_gate_up(d, Is, _ptr(x_row), _ptr(ws13), _ptr(gu), _ptr(h)), "bf_gate_up")
+    return gu, h
+
+
+def bf_down(h_row, ws2):
+    h_row, ws2 = _c(h_row, np.uint16), _c(ws2, np.uint16)
+    d, Is = ws2.shape[0], h_row.shape[0]
+    y = np.empty(d, np.uint16)
+    _chk(lib().orc_bf_down(d, Is, _ptr(h_row), _ptr(ws2), _ptr(y)), "bf_down")
+    return y
 
 
 def shared_row(x_row, ws13, ws2):

@@ -223,24 +223,15 @@ int orc_bucket(int S, int topk, int n_loc, int local_base, const int32_t* ids,
 
 static double silu(double g) { return g / (1.0 + exp(-g)); }
 
-/* One token row through one MXFP4 expert:
+/* gate_up and SwiGLU of one token row through one MXFP4 expert:
  *   gu[n] = bf16( sum_j x[j] * W13[n][j] ),             n < 2I
  *   h[i]  = bf16( silu(gu[i]) * gu[I + i] ),           i < I
- *   y[c]  = bf16( sum_i h[i] * W2[c][i] ),              c < d
- * w13q [2I][d/2], w13s [2I][d/32], w2q [d][I/2], w2s [d][I/32] are this
- * expert's slices. gu and h may be NULL. */
-int orc_expert_row(int d, int I, const uint16_t* x, const uint8_t* w13q,
-                   const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
-                   uint16_t* gu_out, uint16_t* h_out, uint16_t* y) {
-  if (d <= 0 || I <= 0 || (d % 32) || (I % 32) || !x || !w13q || !w13s || !w2q || !w2s || !y)
-    return ORC_EINVAL;
+ * w13q [2I][d/2], w13s [2I][d/32] are this expert's slices; gu may be NULL. */
+int orc_mx_gate_up(int d, int I, const uint16_t* x, const uint8_t* w13q, const uint8_t* w13s,
+                   uint16_t* gu_out, uint16_t* h) {
+  if (d <= 0 || I <= 0 || (d % 32) || !x || !w13q || !w13s || !h) return ORC_EINVAL;
   uint16_t* gu = (uint16_t*)malloc(sizeof(uint16_t) * 2 * (size_t)I);
-  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
-  if (!gu || !h) {
-    free(gu);
-    free(h);
-    return ORC_EINVAL;
-  }
+  if (!gu) return ORC_EINVAL;
   for (int n = 0; n < 2 * I; ++n) {
     const uint8_t* qr = w13q + (long)n * (d / 2);
     const uint8_t* sr = w13s + (long)n * (d / 32);
@@ -252,6 +243,16 @@ int orc_expert_row(int d, int I, const uint16_t* x, const uint8_t* w13q,
     double g = orc_bf16_to_f64(gu[i]), u = orc_bf16_to_f64(gu[I + i]);
     h[i] = orc_f64_to_bf16(silu(g) * u);
   }
+  if (gu_out) memcpy(gu_out, gu, sizeof(uint16_t) * 2 * (size_t)I);
+  free(gu);
+  return ORC_OK;
+}
+
+/* down of one SwiGLU row through one MXFP4 expert:
+ *   y[c] = bf16( sum_i h[i] * W2[c][i] ),  c < d;  w2q [d][I/2], w2s [d][I/32]. */
+int orc_mx_down(int d, int I, const uint16_t* h, const uint8_t* w2q, const uint8_t* w2s,
+                uint16_t* y) {
+  if (d <= 0 || I <= 0 || (I % 32) || !h || !w2q || !w2s || !y) return ORC_EINVAL;
   for (int c = 0; c < d; ++c) {
     const uint8_t* qr = w2q + (long)c * (I / 2);
     const uint8_t* sr = w2s + (long)c * (I / 32);
@@ -259,24 +260,30 @@ int orc_expert_row(int d, int I, const uint16_t* x, const uint8_t* w13q,
     for (int i = 0; i < I; ++i) acc += orc_bf16_to_f64(h[i]) * orc_mx_elem(qr, sr, i);
     y[c] = orc_f64_to_bf16(acc);
   }
-  if (gu_out) memcpy(gu_out, gu, sizeof(uint16_t) * 2 * (size_t)I);
-  if (h_out) memcpy(h_out, h, sizeof(uint16_t) * (size_t)I);
-  free(gu);
-  free(h);
   return ORC_OK;
 }
 
-/* The same chain with dense bf16 weights: ws13 [2 Is][d], ws2 [d][Is]. */
-int orc_shared_row(int d, int Is, const uint16_t* x, const uint16_t* ws13,
-                   const uint16_t* ws2, uint16_t* gu_out, uint16_t* h_out, uint16_t* y) {
-  if (d <= 0 || Is <= 0 || !x || !ws13 || !ws2 || !y) return ORC_EINVAL;
+/* One token row through one MXFP4 expert: gate_up, SwiGLU, down. gu and h may
+ * be NULL. */
+int orc_expert_row(int d, int I, const uint16_t* x, const uint8_t* w13q,
+                   const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
+                   uint16_t* gu_out, uint16_t* h_out, uint16_t* y) {
+  if (I <= 0 || !y) return ORC_EINVAL;
+  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
+  if (!h) return ORC_EINVAL;
+  int rc = orc_mx_gate_up(d, I, x, w13q, w13s, gu_out, h);
+  if (!rc) rc = orc_mx_down(d, I, h, w2q, w2s, y);
+  if (!rc && h_out) memcpy(h_out, h, sizeof(uint16_t) * (size_t)I);
+  free(h);
+  return rc;
+}
+
+/* The same two steps with dense bf16 weights: ws13 [2 Is][d], ws2 [d][Is]. */
+int orc_bf_gate_up(int d, int Is, const uint16_t* x, const uint16_t* ws13, uint16_t* gu_out,
+                   uint16_t* h) {
+  if (d <= 0 || Is <= 0 || !x || !ws13 || !h) return ORC_EINVAL;
   uint16_t* gu = (uint16_t*)malloc(sizeof(uint16_t) * 2 * (size_t)Is);
-  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)Is);
-  if (!gu || !h) {
-    free(gu);
-    free(h);
-    return ORC_EINVAL;
-  }
+  if (!gu) return ORC_EINVAL;
   for (int n = 0; n < 2 * Is; ++n) {
     double acc = 0.0;
     for (int j = 0; j < d; ++j)
@@ -287,17 +294,32 @@ int orc_shared_row(int d, int Is, const uint16_t* x, const uint16_t* ws13,
     double g = orc_bf16_to_f64(gu[i]), u = orc_bf16_to_f64(gu[Is + i]);
     h[i] = orc_f64_to_bf16(silu(g) * u);
   }
+  if (gu_out) memcpy(gu_out, gu, sizeof(uint16_t) * 2 * (size_t)Is);
+  free(gu);
+  return ORC_OK;
+}
+
+int orc_bf_down(int d, int Is, const uint16_t* h, const uint16_t* ws2, uint16_t* y) {
+  if (d <= 0 || Is <= 0 || !h || !ws2 || !y) return ORC_EINVAL;
   for (int c = 0; c < d; ++c) {
     double acc = 0.0;
     for (int i = 0; i < Is; ++i)
       acc += orc_bf16_to_f64(h[i]) * orc_bf16_to_f64(ws2[(long)c * Is + i]);
     y[c] = orc_f64_to_bf16(acc);
   }
-  if (gu_out) memcpy(gu_out, gu, sizeof(uint16_t) * 2 * (size_t)Is);
-  if (h_out) memcpy(h_out, h, sizeof(uint16_t) * (size_t)Is);
-  free(gu);
-  free(h);
   return ORC_OK;
+}
+
+int orc_shared_row(int d, int Is, const uint16_t* x, const uint16_t* ws13,
+                   const uint16_t* ws2, uint16_t* gu_out, uint16_t* h_out, uint16_t* y) {
+  if (Is <= 0 || !y) return ORC_EINVAL;
+  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)Is);
+  if (!h) return ORC_EINVAL;
+  int rc = orc_bf_gate_up(d, Is, x, ws13, gu_out, h);
+  if (!rc) rc = orc_bf_down(d, Is, h, ws2, y);
+  if (!rc && h_out) memcpy(h_out, h, sizeof(uint16_t) * (size_t)Is);
+  free(h);
+  return rc;
 }
 
 /* Every bucket row through its expert, then (Is > 0) every token through the

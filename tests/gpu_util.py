@@ -11,13 +11,14 @@ Tolerances (derived from the arithmetic; every comparison states its own):
   correct); weights within 1e-6 relative of the oracle's weights computed
   from the GPU's own logits;
 * buckets: bit-exact;
-* expert outputs y: the GPU accumulates in fp32 before each bf16 rounding,
-  the oracle in fp64, so a value sitting on a bf16 rounding boundary can land
-  one ulp apart and move later sums slightly: per row, max |dy| <= 1e-2 RMS(y)
-  and at least 90 % of the bf16 values identical;
+* expert FFN, step by step: the GPU's SwiGLU rows h against the oracle's
+  gate_up + SwiGLU (compare_h), then the GPU's y against the oracle's down GEMM
+  applied to the GPU's own h (compare_y_step); the bounds are stated there;
 * combine alone (same y): fp32 against fp64, max |d out| <= 1e-5 RMS(out);
-* end to end: max |d out| <= 2e-2 RMS(out_oracle) over the compared rows;
-  rows the oracle gives exactly zero must be exactly zero.
+* end to end: max |d out| <= 2e-2 RMS(out_oracle) over the compared rows on
+  the named workloads; synthetic small-dimension cases add two bf16 ulps of
+  each contributing term (check_block explains why); rows the oracle gives
+  exactly zero must be exactly zero.
 """
 
 from __future__ import annotations
@@ -86,32 +87,102 @@ def check_bucket(inp, g) -> dict:
     return bk
 
 
-def oracle_y_rows(inp, bk, rows_sel) -> dict:
-    """Oracle expert outputs of the chosen bucket rows: {row: y bf16 bits}."""
+def gpu_h(g, cfg) -> tuple[np.ndarray, np.ndarray | None]:
+    """The SwiGLU rows the FFN left in its workspace: routed [R_max][I] and,
+    with a shared expert, [S][I_s]."""
+    ws = to_np(g["blk"].ws)
+    R = cfg.S * min(cfg.topk, cfg.n_local)
+    nb = R * cfg.I * 2
+    h = ws[:nb].view(np.uint16).reshape(R, cfg.I)
+    hs = None
+    if cfg.shared_I:
+        off = (nb + 255) // 256 * 256
+        hs = ws[off : off + cfg.S * cfg.shared_I * 2].view(np.uint16).reshape(cfg.S, cfg.shared_I)
+    return h, hs
+
+
+def compare_h(h_gpu, h_orc, what=""):
+    """SwiGLU rows. The GPU rounds fp32 sums of gate_up to bf16 where the oracle
+    rounds fp64 sums, so a gate or up value sitting on a bf16 rounding boundary
+    can land one ulp apart (measured: ~0.1 % of values), and silu amplifies that
+    for large negative gates, whose outputs are tiny. Below a gate of about -88,
+    exp(-g) overflows fp32 and the GPU's SwiGLU value is 0 where the oracle's is
+    ~1e-37 or less: numerically zero next to the row. So: per element
+    |dh| <= 2^-6 |h| + 2^-10 RMS(h), and >= 98 % bit-identical among the values
+    with |h| >= 2^-24 RMS(h)."""
+    a, b = bf16_val(h_gpu), bf16_val(h_orc)
+    rms = np.sqrt(np.mean(b * b))
+    err = np.abs(a - b)
+    tol = 2.0**-6 * np.abs(b) + 2.0**-10 * rms
+    bad = np.flatnonzero(err > tol)
+    assert bad.size == 0, f"{what}: {bad.size} values off, e.g. [{bad[0]}] {a[bad[0]]} vs {b[bad[0]]}"
+    sig = np.abs(b) >= 2.0**-24 * rms
+    same = np.mean(h_gpu[sig] == h_orc[sig]) if sig.any() else 1.0
+    assert same >= 0.98, f"{what}: only {same:.4f} of bf16 values identical"
+
+
+def compare_y_step(y_gpu, y_ref, h_gpu, w_dense, what=""):
+    """Down GEMM on the same (GPU) SwiGLU row: the only differences are the fp32
+    accumulation order and a bf16 rounding flip it can cause:
+    |dy| <= 2^-7 |y| + (K/32 + 64) 2^-24 sum_i |h_i w_ci|, >= 99 % identical."""
+    a, b = bf16_val(y_gpu), bf16_val(y_ref)
+    hv = bf16_val(h_gpu)
+    mag = np.abs(w_dense) @ np.abs(hv)
+    K = hv.shape[0]
+    tol = 2.0**-7 * np.abs(b) + (K / 32 + 64) * 2.0**-24 * mag
+    err = np.abs(a - b)
+    bad = np.flatnonzero(err > tol)
+    assert bad.size == 0, f"{what}: {bad.size} values off, e.g. [{bad[0]}] {a[bad[0]]} vs {b[bad[0]]}"
+    same = np.mean(y_gpu == y_ref)
+    assert same >= 0.99, f"{what}: only {same:.4f} of bf16 values identical"
+
+
+def check_ffn_rows(inp, g, bk, rows_sel) -> dict:
+    """Step-wise parity of the chosen bucket rows; returns the oracle's own
+    end-to-end y rows {row: y}."""
+    from tests._ref import decode_mx
+
     cfg = inp["cfg"]
-    out = {}
+    h_all, _ = gpu_h(g, cfg)
+    dense = {}
+    y_o = {}
     for r in rows_sel:
         el = int(np.searchsorted(bk["offsets"], r, side="right") - 1)
         t = int(bk["rows"][r])
-        _, _, y = oracle.expert_row(
-            inp["x"][t], inp["w13q"][el], inp["w13s"][el], inp["w2q"][el], inp["w2s"][el]
-        )
-        out[int(r)] = y
-    return out
+        _, h_o = oracle.mx_gate_up(inp["x"][t], inp["w13q"][el], inp["w13s"][el])
+        compare_h(h_all[r], h_o, f"h of bucket row {r} (expert {el}, token {t})")
+        if el not in dense:
+            dense[el] = decode_mx(inp["w2q"][el], inp["w2s"][el])
+        y_ref = oracle.mx_down(h_all[r], inp["w2q"][el], inp["w2s"][el])
+        compare_y_step(g["y"][r], y_ref, h_all[r], dense[el], f"y of bucket row {r}")
+        y_o[int(r)] = oracle.mx_down(h_o, inp["w2q"][el], inp["w2s"][el])
+    return y_o
 
 
-def compare_y(y_gpu_row, y_orc_row, what=""):
-    a = bf16_val(y_gpu_row)
-    b = bf16_val(y_orc_row)
-    rms = np.sqrt(np.mean(b * b))
-    err = np.abs(a - b).max()
-    same = np.mean(y_gpu_row == y_orc_row)
-    assert err <= 1e-2 * rms + 1e-30, f"{what}: max |dy| {err:.3g} > 1e-2 rms {rms:.3g}"
-    assert same >= 0.9, f"{what}: only {same:.3f} of bf16 values identical"
+def check_shared_rows(inp, g, tokens) -> dict:
+    cfg = inp["cfg"]
+    R = cfg.S * min(cfg.topk, cfg.n_local)
+    _, hs = gpu_h(g, cfg)
+    w2 = bf16_val(inp["ws2"])
+    y_o = {}
+    for t in tokens:
+        _, h_o = oracle.bf_gate_up(inp["x"][t], inp["ws13"])
+        compare_h(hs[t], h_o, f"shared h of token {t}")
+        y_ref = oracle.bf_down(hs[t], inp["ws2"])
+        compare_y_step(g["y"][R + t], y_ref, hs[t], w2, f"shared y of token {t}")
+        y_o[t] = oracle.bf_down(h_o, inp["ws2"])
+    return y_o
 
 
-def check_block(inp, g, tokens=None, max_rows=None) -> None:
-    """Everything, step by step, on all tokens or on ``tokens`` only."""
+def check_block(inp, g, tokens=None, strict=True) -> None:
+    """Everything, step by step, on all tokens or on ``tokens`` only.
+
+    End to end, ``strict`` applies the plain bound max |d out| <= 2e-2 RMS(out).
+    Otherwise (synthetic small-dimension cases) each element may also move by
+    two bf16 ulps of every term that reaches it, 2^-7 (sum_s w_s |z_s| + |y_sh|):
+    one legitimate rounding flip at a bf16 hand-off moves an expert output by an
+    ulp, and an element several times the output RMS then exceeds the plain
+    bound on its own."""
     cfg = inp["cfg"]
     lo = check_logits(inp, g)
     check_topk(inp, g, lo)
@@ -119,38 +190,42 @@ def check_block(inp, g, tokens=None, max_rows=None) -> None:
     S = cfg.S
     tokens = list(range(S)) if tokens is None else list(tokens)
     R = cfg.S * min(cfg.topk, cfg.n_local)
-    # expert outputs of the picks of the chosen tokens
+    # expert FFN of the picks of the chosen tokens, step by step
     sel = sorted({int(p) for t in tokens for p in bk["pick_pos"][t] if p >= 0})
-    if max_rows is not None:
-        sel = sel[:max_rows]
-    yo = oracle_y_rows(inp, bk, sel)
-    for r, y in yo.items():
-        compare_y(g["y"][r], y, f"bucket row {r}")
-    y_full = g["y"].copy()
-    if cfg.shared_I:
-        for t in tokens:
-            _, _, ys = oracle.shared_row(inp["x"][t], inp["ws13"], inp["ws2"])
-            compare_y(g["y"][R + t], ys, f"shared row {t}")
+    yo = check_ffn_rows(inp, g, bk, sel)
+    ys = check_shared_rows(inp, g, tokens) if cfg.shared_I else {}
     # combine alone: oracle on the GPU's y and weights
-    out_c = oracle.combine(cfg, y_full, g["w"], g["pick_pos"], inp.get("gamma"))
+    out_c = oracle.combine(cfg, g["y"], g["w"], g["pick_pos"], inp.get("gamma"))
     for t in tokens:
         rms = np.sqrt(np.mean(out_c[t].astype(np.float64) ** 2))
         err = np.abs(g["out"][t] - out_c[t]).max()
         assert err <= 1e-5 * rms + 1e-30, f"combine token {t}: {err:.3g} vs rms {rms:.3g}"
-    # end to end on the selected tokens: oracle y and weights from its logits
+    # end to end on the chosen tokens: the oracle's own chain (y from its own
+    # SwiGLU rows, weights from its own logits) on the GPU's routing choice
     y_o = np.zeros_like(g["y"])
     for r, y in yo.items():
         y_o[r] = y
-    if cfg.shared_I:
-        for t in tokens:
-            y_o[R + t] = oracle.shared_row(inp["x"][t], inp["ws13"], inp["ws2"])[2]
+    for t, y in ys.items():
+        y_o[R + t] = y
     w_o = oracle.route_weights(lo, g["ids"], cfg.renorm)
     out_o = oracle.combine(cfg, y_o, w_o, g["pick_pos"], inp.get("gamma"))
     ref = out_o[tokens].astype(np.float64)
     got = g["out"][tokens].astype(np.float64)
     rms = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
-    if max_rows is None:
-        err = np.abs(got - ref).max() if ref.size else 0.0
-        assert err <= 2e-2 * rms + 1e-30, f"end to end: max |d out| {err:.3g} > 2e-2 RMS {rms:.3g}"
-        zero = np.all(ref == 0, axis=1)
-        assert np.all(got[zero] == 0), "tokens without a local pick must be exactly zero"
+    err = np.abs(got - ref)
+    bound = np.full_like(ref, 2e-2 * rms + 1e-30)
+    if not strict:
+        eps = float(np.float32(cfg.eps))
+        for i, t in enumerate(tokens):
+            for s_, p in enumerate(g["pick_pos"][t]):
+                if p >= 0:
+                    z = oracle.norm_row(y_o[p], inp.get("gamma"), eps)
+                    bound[i] += 2.0**-7 * abs(float(w_o[t, s_])) * np.abs(z)
+            if cfg.shared_I:
+                bound[i] += 2.0**-7 * np.abs(bf16_val(y_o[R + t]))
+    worst = np.unravel_index(np.argmax(err - bound), err.shape) if err.size else None
+    assert np.all(err <= bound), (
+        f"end to end: |d out| {err[worst]:.3g} > bound {bound[worst]:.3g} (2e-2 RMS = {2e-2 * rms:.3g})"
+    )
+    zero = np.all(ref == 0, axis=1)
+    assert np.all(got[zero] == 0), "tokens without a local pick must be exactly zero"

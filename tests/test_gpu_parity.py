@@ -68,7 +68,7 @@ def test_pack_mxfp4_is_a_permutation():
 @pytest.mark.parametrize("gamma", ["ones", "random"])
 def test_tiny_block(seed, gamma):
     inp = make_inputs(get_config("tiny"), seed, gamma=gamma)
-    check_block(inp, run_gpu(inp))
+    check_block(inp, run_gpu(inp), strict=True)
 
 
 EDGE = {
@@ -93,7 +93,7 @@ EDGE = {
 @pytest.mark.parametrize("name", list(EDGE))
 def test_edge_cases(name):
     inp = make_inputs(EDGE[name], 11, gamma="random")
-    check_block(inp, run_gpu(inp))
+    check_block(inp, run_gpu(inp), strict=False)
 
 
 def test_no_local_picks_gives_zero():
@@ -102,7 +102,7 @@ def test_no_local_picks_gives_zero():
     g = run_gpu(inp)
     assert g["active"][0] == 0 and np.all(g["counts"] == 0)
     assert np.all(g["out"] == 0)
-    check_block(inp, g)
+    check_block(inp, g, strict=True)
 
 
 def test_deterministic():
@@ -140,4 +140,4 @@ def test_full_workload(name, n_tok):
     cfg = get_config(name)
     inp = make_inputs(cfg, 0, gamma="random")
     g = run_gpu(inp)
-    check_block(inp, g, tokens=_sample_tokens(g, cfg, n_tok))
+    check_block(inp, g, tokens=_sample_tokens(g, cfg, n_tok), strict=True)
