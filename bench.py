@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the local-expert MoE block on one MI355X.
 
-A step is one pass of the whole block -- moe_route -> moe_bucket ->
-moe_expert_ffn -> moe_combine -- over one batch of S token rows, all inputs
-resident in HBM. The default workload is S = 8, d = 4096, 256 experts (32
-local), I = 2048, top-8 uniform routing ("s8_uniform").
+A step is one pass of the whole block -- route, bucket, expert FFN, combine --
+over one batch of S token rows, all inputs resident in HBM. It is timed as the
+library's single-launch entry point moe_forward (the headline `value`) and, for
+comparison, as the four calls moe_route -> moe_bucket -> moe_expert_ffn ->
+moe_combine. The default workload is S = 8, d = 4096, 256 experts (32 local),
+I = 2048, top-8 uniform routing ("s8_uniform").
 
 Last-level-cache control: MI355X's 256 MB Infinity Cache would hold one
 step's active weights (about 94 MB here), so the benchmark keeps R copies of
@@ -13,9 +15,10 @@ step by step; every step then streams its weights from HBM, as a decode step
 does between the other layers' weights.
 
 Output: one JSON line (see the fields below). ``roofline`` covers the
-dominant call, moe_expert_ffn, timed with HIP events on its stream in a second
-timed pass; its ``traffic`` comes from the committed rocprofv3 counter summary
-when that summary was taken on the current FFN source, else null.
+dominant kernel, the moe_forward launch (the only kernel of a step), timed with
+HIP events around each launch on its stream in a separate timed pass; its
+``traffic`` comes from the committed rocprofv3 counter summary when that summary
+was taken on the current kernel sources, else null.
 ``cpu_baseline`` times the CPU oracle on the same workload.
 """
 
@@ -35,27 +38,30 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 LLC_BYTES = 256 * 2**20  # MI355X Infinity Cache
-FFN_SOURCES = ["moe_decode_layer_router_amd/csrc/ffn.hip", "moe_decode_layer_router_amd/csrc/common.h"]
+KERNEL_SOURCES = [
+    "moe_decode_layer_router_amd/csrc/" + f
+    for f in ("forward.hip", "ffn_dev.h", "route_dev.h", "bucket_dev.h", "combine_dev.h", "common.h")
+]
 
 
-def ffn_source_sha() -> str:
+def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for p in FFN_SOURCES:
+    for p in KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def committed_traffic(workload: str):
-    """HBM bytes a moe_expert_ffn call moves, from profiles/, if taken on the
-    current FFN source (else None)."""
-    p = os.path.join(ROOT, "profiles", f"expert_ffn_{workload}_traffic.md")
+    """HBM bytes one moe_forward launch moves, from profiles/, if taken on the
+    current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", f"moe_forward_{workload}_traffic.md")
     if not os.path.exists(p):
         return None
     txt = open(p).read()
-    m_sha = re.search(r"ffn_source_sha:\s*([0-9a-f]+)", txt)
-    m_b = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", txt)
-    if not m_sha or not m_b or m_sha.group(1) != ffn_source_sha():
+    m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_sha():
         return None
     return float(m_b.group(1))
 
@@ -118,7 +124,7 @@ def main() -> int:
     inp = make_inputs(cfg, 0)
     torch.cuda.set_device(0)
     blk = MoeBlock(inp, device="cuda:0")
-    blk.step(0)
+    blk.forward(0)
     torch.cuda.synchronize()
     counts = blk.counts.cpu().numpy()
     n_active = int((counts > 0).sum())
@@ -140,45 +146,45 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    for i in range(args.warmup):
-        blk.step(i % copies)
-    torch.cuda.synchronize()
-
-    # timed pass 1: whole steps
     K = args.steps
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(K):
-        blk.step(i % copies)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / K
 
-    # timed pass 2: the expert FFN call alone, events on its stream
+    def timed(fn) -> float:
+        for i in range(args.warmup):
+            fn(i % copies)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(K):
+            fn(i % copies)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / K
+
+    # timed pass 1: whole steps, one launch each (the headline)
+    ms = timed(blk.forward)
+    # timed pass 2: whole steps as the four calls
+    ms4 = timed(blk.step)
+    # timed pass 3: each launch bracketed by events on its stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
-        s = i % copies
-        blk.route(s)
-        blk.bucket()
         evs[i][0].record()
-        blk.expert_ffn(s)
+        blk.forward(i % copies)
         evs[i][1].record()
-        blk.combine()
     torch.cuda.synchronize()
-    ffn_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    assert blk.forward_error() == 0, "a wait in the fused launch hit its bound"
 
-    R = blk.dims.r_max
-    # algorithmic bytes of one moe_expert_ffn call: the active experts' MXFP4
-    # weights, the shared expert's bf16 weights, x read, h written and read,
-    # y written
-    b_act = cfg.S * cfg.d * 2 + picks * cfg.I * 2 * 2 + picks * cfg.d * 2
+    # algorithmic bytes of one launch: the router weights, the active experts'
+    # MXFP4 weights, the shared expert's bf16 weights, x read, h written and
+    # read, y written and read, logits written and read, out written
+    b_act = cfg.S * cfg.d * 2 + picks * cfg.I * 2 * 2 + picks * cfg.d * 2 * 2
+    b_act += cfg.S * cfg.E * 4 * 2 + cfg.S * cfg.d * 4
     if cfg.shared_I:
-        b_act += cfg.S * cfg.shared_I * 2 * 2 + cfg.S * cfg.d * 2
-    ffn_bytes = b_mx + b_shared + b_act
-    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+        b_act += cfg.S * cfg.shared_I * 2 * 2 + cfg.S * cfg.d * 2 * 2
+    launch_bytes = b_step_w + b_act
+    achieved = launch_bytes / (kern_ms * 1e-3) / 1e9
     traffic = committed_traffic(cfg.name)
 
     tok_s = cfg.S / (ms * 1e-3)
@@ -193,7 +199,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4 weights -> bf16 MFMA, fp32 accumulation",
+        "dtype": "bf16",
         "data": "synthetic (seeded generator, seed 0)",
         "config": {
             "workload": cfg.name,
@@ -210,18 +216,17 @@ def main() -> int:
         },
         "mxfp4_weight_gbps": round(b_mx / (ms * 1e-3) / 1e9, 1),
         "all_weight_pct_hbm_peak": round(100 * b_step_w / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "four_call_ms_per_step": round(ms4, 5),
         "roofline": {
-            "kernel": "moe_expert_ffn (gate_up + down launches"
-            + (", shared expert launches" if cfg.shared_I else "")
-            + ")",
+            "kernel": "moe_forward_kernel (the whole step in one launch)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": ffn_bytes,
-            "avg_ms": round(ffn_ms, 5),
+            "algorithmic_bytes": launch_bytes,
+            "avg_ms": round(kern_ms, 5),
         },
         "cpu_baseline": None,
     }

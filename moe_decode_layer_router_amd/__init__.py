@@ -31,6 +31,8 @@ __all__ = [
     "moe_ffn_workspace_bytes",
     "moe_expert_ffn",
     "moe_combine",
+    "moe_forward_workspace_bytes",
+    "moe_forward",
     "MOE_W13",
     "MOE_W2",
 ]
@@ -102,7 +104,13 @@ def lib() -> ctypes.CDLL:
         L.moe_bucket.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P]
         L.moe_expert_ffn.argtypes = [_DP] + [_P] * 11 + [ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [_DP, _P, _P, _P, _P, _P, _P]
-        for f in ("moe_pack_mxfp4", "moe_pack_bf16", "moe_route", "moe_bucket", "moe_expert_ffn", "moe_combine"):
+        L.moe_forward_workspace_bytes.argtypes = [_DP]
+        L.moe_forward_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_forward.argtypes = [_DP] + [_P] * 19 + [ctypes.c_size_t, _P]
+        for f in (
+            "moe_pack_mxfp4", "moe_pack_bf16", "moe_route", "moe_bucket", "moe_expert_ffn", "moe_combine",
+            "moe_forward",
+        ):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -215,4 +223,21 @@ def moe_combine(dims, y, topk_w, pick_pos, gamma, out, stream=None) -> None:
     _call(
         "moe_combine", ctypes.byref(_d(dims)), _ptr(y), _ptr(topk_w), _ptr(pick_pos), _ptr(gamma), _ptr(out),
         _stream(stream),
+    )
+
+
+def moe_forward_workspace_bytes(dims) -> int:
+    return lib().moe_forward_workspace_bytes(ctypes.byref(_d(dims)))
+
+
+def moe_forward(dims, x, w_router, bias, w13_packed, w2_packed, ws13_packed, ws2_packed, gamma, logits,
+                topk_ids, topk_w, counts, offsets, rows, pick_pos, active, y, out, workspace,
+                workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _call(
+        "moe_forward", ctypes.byref(_d(dims)), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13_packed),
+        _ptr(w2_packed), _ptr(ws13_packed), _ptr(ws2_packed), _ptr(gamma), _ptr(logits), _ptr(topk_ids),
+        _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(rows), _ptr(pick_pos), _ptr(active), _ptr(y), _ptr(out),
+        _ptr(workspace), int(workspace_bytes), _stream(stream),
     )

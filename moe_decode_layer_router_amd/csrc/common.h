@@ -92,12 +92,41 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// cache-policy operand of the buffer intrinsics: sc1 = device-scope coherent
+constexpr int kCpolSc1 = 16;
+
 template <typename T>
 __device__ __forceinline__ T ld_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// fp64 -> bf16 bits, round to nearest even, without double rounding: the
+// value is first rounded to fp32 "to odd" (an inexact result gets its last
+// significand bit set), which keeps enough information for the final rounding.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double v) {
+  if (v != v) return 0x7fc0u;
+  const float f = static_cast<float>(v);  // nearest fp32
+  uint32_t u = __float_as_uint(f);
+  if (static_cast<double>(f) != v && (u & 0x7f800000u) != 0x7f800000u) {
+    if (f == 0.0f) {
+      u |= 1u;  // below the smallest subnormal: an odd neighbour of zero
+    } else if ((u & 1u) == 0u) {
+      const bool away = (v > static_cast<double>(f)) == (f > 0.0f);  // toward v = larger magnitude?
+      u = away ? u + 1u : u - 1u;
+    }
+  }
+  return f32_to_bf16_bits(__uint_as_float(u));
+}
+
+// SwiGLU of one gate / up pair of bf16 values, evaluated in fp64 and rounded
+// once to bf16: silu(g) * u with silu(g) = g / (1 + exp(-g)). In fp32, 1 + exp(-g)
+// is exactly 1 above g ~ 17 and exp(-g) overflows below g ~ -88, which would move
+// results across bf16 rounding boundaries; fp64 keeps the elementwise rounding
+// of the exact product.
+__device__ __forceinline__ uint32_t swiglu_bf16_bits(float g, float u) {
+  const double gd = g;
+  return f64_to_bf16_bits(gd / (1.0 + exp(-gd)) * static_cast<double>(u));
+}
 
 // wave-wide sum, every lane gets the total; fixed butterfly order
 __device__ __forceinline__ float wave_sum(float v) {

@@ -1,0 +1,296 @@
+// ffn_dev.h -- one task of the expert GEMMs (gate_up + SwiGLU, or down) as a
+// workgroup-level device function, used by the moe_expert_ffn kernels and the
+// fused kernel.
+//
+// Muse Spark K3 page, stages "C, D": gate_up and down of the local experts with
+// MXFP4 weights decoded in registers and fed to bf16 MFMA; functions "mx_chunk"
+// and "fp4_mma": a 16-row MXFP4 group is processed in 256-K chunks of 8 MFMA
+// steps with one e8m0 scale per 32 K; "task_ring": compute one task while the
+// next ones' loads are in flight. K5 page: every row tile is 16 tokens (the
+// MFMA N dimension). The Kimi-K3 layer page's shared expert ("k2_launch": w_sgu,
+// w_sd) runs the same chain on dense bf16 weights.
+//
+// A task: 64 weight rows (4 MFMA row tiles) of one expert against one group of
+// up to 16 * TTG bucket rows, over the full K. The workgroup's 4 waves split K:
+// wave w takes chunks c = w, w + 4, ... of 128 K, so together they stream the
+// task's packed tiles front to back. Each wave keeps P chunks of loads in
+// flight (weights non-temporal, activations through the cache), decodes MXFP4
+// with the scaled fp4 -> bf16 converts and accumulates with
+// v_mfma_f32_16x16x32_bf16. The four partial tiles are summed through LDS in
+// wave order (deterministic); the epilogue rounds to bf16 and, for gate_up,
+// applies SwiGLU in registers (the packed row order gives each lane matching
+// gate and up rows).
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace moeblk {
+
+constexpr int kSplit = 4;  // waves a workgroup, = row tiles a task
+
+// Work items enumerate, for the local experts in order, their groups of
+// G = 16 * TTG bucket rows (an expert without picks has none). Wave-level:
+// lane u holds expert u's count `cnt` (0 for u >= n_loc); wave prefix sums of
+// the group counts and of the counts give the item's expert and its first
+// bucket row (the bucket offsets are the exclusive prefix sums of the counts).
+// Returns false past the last item.
+template <int TTG>
+__device__ __forceinline__ bool find_task(int cnt, int wi, int& el, int& row0, int& ntok) {
+  constexpr int G = 16 * TTG;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ng = (cnt + G - 1) / G;
+  int incl_ng = ng, incl_cnt = cnt;  // inclusive scans over lanes 0..31
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    const int o1 = __shfl_up(incl_ng, m, kWave);
+    const int o2 = __shfl_up(incl_cnt, m, kWave);
+    if (lane >= m) {
+      incl_ng += o1;
+      incl_cnt += o2;
+    }
+  }
+  const uint64_t hit = __ballot(lane < 32 && wi < incl_ng);
+  if (hit == 0) return false;
+  const int u = __builtin_ctzll(hit);
+  const int g = wi - (__shfl(incl_ng, u, kWave) - __shfl(ng, u, kWave));
+  const int c = __shfl(cnt, u, kWave);
+  el = u;
+  row0 = __shfl(incl_cnt, u, kWave) - c + g * G;
+  ntok = min(G, c - g * G);
+  return true;
+}
+
+// Work items of all local experts (wave-level, every lane gets it).
+template <int TTG>
+__device__ __forceinline__ int count_work(int cnt) {
+  constexpr int G = 16 * TTG;
+  int ng = (cnt + G - 1) / G;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ng += __shfl_xor(ng, m, kWave);
+  return ng;
+}
+
+template <int TTG>
+struct MxChunk {
+  u32x4_t w[4];       // 4 row tiles x 32 e2m1 codes a lane
+  uint32_t s;         // the 4 row tiles' e8m0 bytes
+  u32x4_t b[TTG][4];  // activations: 32 bf16 a lane a token tile
+};
+
+template <int TTG>
+struct BfChunk {
+  u32x4_t w[4][4];  // 4 row tiles x 4 MFMA steps x 8 bf16
+  u32x4_t b[TTG][4];
+};
+
+// Activation (B) rows of a task. Loads are unconditional (every token tile,
+// clamped chunk indices): the waitcnt insertion then sees one fixed issue order
+// and keeps the ring in flight. With kCoh the loads carry the device-scope
+// coherence bit (sc1): rows written earlier in the same launch by another XCD
+// are read from the coherence point, not from a stale line of this XCD's L2.
+template <int TTG, bool kCoh>
+struct BRows {
+  const uint16_t* bp[TTG];         // !kCoh: this lane's row pointers (+ its K group)
+  __amdgpu_buffer_rsrc_t rsrc;     // kCoh: buffer over the B rows
+  uint32_t boff[TTG];              // kCoh: this lane's byte offsets
+
+  __device__ __forceinline__ void init(const uint16_t* bsrc, int K, const int (&src)[TTG], int g) {
+    if constexpr (kCoh) {
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(bsrc), 0, 0x7fffffff,
+                                               0x00020000);
+#pragma unroll
+      for (int tt = 0; tt < TTG; ++tt) boff[tt] = (static_cast<uint32_t>(src[tt]) * K + 32 * g) * 2u;
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < TTG; ++tt) bp[tt] = bsrc + static_cast<size_t>(src[tt]) * K + 32 * g;
+    }
+  }
+
+  __device__ __forceinline__ void load(u32x4_t (&b)[TTG][4], int c) const {
+#pragma unroll
+    for (int tt = 0; tt < TTG; ++tt) {
+      if constexpr (kCoh) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          b[tt][q] = __builtin_amdgcn_raw_buffer_load_b128(
+              rsrc, boff[tt] + static_cast<uint32_t>(c * kChunkK + 8 * q) * 2u, 0, kCpolSc1);
+      } else {
+        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(bp[tt] + c * kChunkK);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[tt][q] = p[q];
+      }
+    }
+  }
+};
+
+template <int TTG>
+__device__ __forceinline__ void load_w(MxChunk<TTG>& ch, const uint8_t* wlane, const uint8_t* slane,
+                                       int c) {
+  const uint8_t* t = wlane + static_cast<size_t>(c) * kMxTileBytes;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ch.w[r] = ld_nt<u32x4_t>(t + r * 1024);
+  ch.s = ld_nt<uint32_t>(slane + static_cast<size_t>(c) * kMxTileBytes);
+}
+
+template <int TTG>
+__device__ __forceinline__ void load_w(BfChunk<TTG>& ch, const uint8_t* wlane, const uint8_t*,
+                                       int c) {
+  const uint8_t* t = wlane + static_cast<size_t>(c) * kBfTileBytes;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ch.w[r][q] = ld_nt<u32x4_t>(t + r * 4096 + q * 1024);
+}
+
+template <int TTG>
+__device__ __forceinline__ void compute_chunk(const MxChunk<TTG>& ch, f32x4_t (&acc)[TTG][4],
+                                              int n_tt) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float sc = e8m0_scale((ch.s >> (8 * r)) & 0xffu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8_t av = decode_fp4x8(ch.w[r][q], sc);
+#pragma unroll
+      for (int tt = 0; tt < TTG; ++tt)
+        if (tt < n_tt)
+          acc[tt][r] = mfma_bf16(av, __builtin_bit_cast(bf16x8_t, ch.b[tt][q]), acc[tt][r]);
+    }
+  }
+}
+
+template <int TTG>
+__device__ __forceinline__ void compute_chunk(const BfChunk<TTG>& ch, f32x4_t (&acc)[TTG][4],
+                                              int n_tt) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, ch.w[r][q]);
+#pragma unroll
+      for (int tt = 0; tt < TTG; ++tt)
+        if (tt < n_tt)
+          acc[tt][r] = mfma_bf16(av, __builtin_bit_cast(bf16x8_t, ch.b[tt][q]), acc[tt][r]);
+    }
+}
+
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
+// Workgroup-level (4 waves). tiles: the packed tiles of (expert, row block rb);
+// B rows: src_of(r) for bucket rows r = row0 .. row0 + ntok - 1 (row length K;
+// gate_up: token rows of x; down: SwiGLU rows, read with the coherence bit);
+// out: output rows indexed by bucket row (row length out_ld; gate_up writes its
+// SwiGLU rows through to the coherence point); before_b() runs
+// after the weight prefetch and before the first activation load; red: LDS.
+template <bool kMx, int TTG, int P, bool kGateUp, class SrcOf, class BeforeB>
+__device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int NC,
+                                         const uint16_t* __restrict__ bsrc, int K, int row0,
+                                         int ntok, int rb, uint16_t* __restrict__ out, int out_ld,
+                                         SrcOf src_of, BeforeB before_b,
+                                         f32x4_t (*red)[TTG][4][kWave]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int n_tt = (ntok + 15) / 16;
+  const uint8_t* wlane = tiles + lane * 16;
+  const uint8_t* slane = tiles + 4096 + lane * 4;
+
+  // this lane's B rows (token tile tt, column col); columns past the group's
+  // rows repeat its last row and are never stored. The row lookup is issued
+  // before the weights so that waiting for it leaves them in flight.
+  int src[TTG];
+#pragma unroll
+  for (int tt = 0; tt < TTG; ++tt) src[tt] = src_of(row0 + min(tt * 16 + col, ntok - 1));
+
+  using Chunk = typename std::conditional<kMx, MxChunk<TTG>, BfChunk<TTG>>::type;
+  const int my_n = (NC - w + kSplit - 1) / kSplit;  // this wave's chunks: w, w + 4, ...
+  Chunk ring[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) load_w<TTG>(ring[i], wlane, slane, min(w + kSplit * i, NC - 1));
+
+  before_b();
+
+  BRows<TTG, !kGateUp> bp;  // down tasks read SwiGLU rows written in this launch
+  bp.init(bsrc, K, src, g);
+#pragma unroll
+  for (int i = 0; i < P; ++i) bp.load(ring[i].b, min(w + kSplit * i, NC - 1));
+
+  f32x4_t acc[TTG][4];
+#pragma unroll
+  for (int tt = 0; tt < TTG; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[tt][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  int j0 = 0;
+  for (; j0 + 2 * P <= my_n; j0 += P) {  // steady state: every refill is needed
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      compute_chunk<TTG>(ring[i], acc, n_tt);
+      const int c = w + kSplit * (j0 + i + P);
+      load_w<TTG>(ring[i], wlane, slane, c);
+      bp.load(ring[i].b, c);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {  // fewer than 2P chunks left
+    if (j0 + i < my_n) {
+      compute_chunk<TTG>(ring[i], acc, n_tt);
+      if (j0 + i + P < my_n) {
+        const int c = w + kSplit * (j0 + i + P);
+        load_w<TTG>(ring[i], wlane, slane, c);
+        bp.load(ring[i].b, c);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (j0 + P + i < my_n) compute_chunk<TTG>(ring[i], acc, n_tt);
+
+  // sum the 4 waves' partial tiles in wave order
+  __syncthreads();  // the previous task's epilogue has read red
+#pragma unroll
+  for (int tt = 0; tt < TTG; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[w][tt][r][lane] = acc[tt][r];
+  __syncthreads();
+
+  const int r = w;  // this thread finishes row tile r, MFMA lane `lane`
+#pragma unroll
+  for (int tt = 0; tt < TTG; ++tt) {
+    if (tt >= n_tt) break;
+    f32x4_t s = red[0][tt][r][lane];
+#pragma unroll
+    for (int ww = 1; ww < kSplit; ++ww) s += red[ww][tt][r][lane];
+    const int c = tt * 16 + col;
+    if (c >= ntok) continue;
+    uint16_t* orow = out + static_cast<size_t>(row0 + c) * out_ld;
+    if constexpr (kGateUp) {
+      // rows 4g..4g+3 of tile r: gate i, gate i+1, up i, up i+1
+      const float g0 = round_bf16(s[0]), g1 = round_bf16(s[1]);
+      const float u0 = round_bf16(s[2]), u1 = round_bf16(s[3]);
+      const int i0 = 32 * rb + 8 * r + 2 * g;
+      // written through to the coherence point (sc1): down tasks of this launch
+      // on other XCDs read it
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(orow + i0),
+                         swiglu_bf16_bits(g0, u0) | (swiglu_bf16_bits(g1, u1) << 16),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
+      *reinterpret_cast<u32x2_t*>(orow + n0) =
+          u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+    }
+  }
+}
+
+// upper bound of the work items: sum over experts of ceil(count / G)
+inline int max_work(int R_max, int n_loc, int G) {
+  const int experts = n_loc < R_max ? n_loc : R_max;
+  return experts + R_max / G;
+}
+
+}  // namespace moeblk

@@ -1,0 +1,86 @@
+// forward.hip -- moe_forward: the whole block as four launches on one stream.
+//
+//   1  router logits (one workgroup an expert row)
+//   2  top-k of every token and the bucketing, in one workgroup
+//   3  the expert FFNs (gate_up, SwiGLU, down, shared expert) in one launch
+//   4  per-pick RMSNorm and the weighted sum (one workgroup a token)
+//
+// The outputs are those of moe_route, moe_bucket, moe_expert_ffn and
+// moe_combine, bit for bit: the same device code runs in the same order.
+// Steps 2 and 3 each replace two launches of the four-call path. (Measured on
+// MI355X: a launch costs about 2.5 us, while a grid-wide barrier across all
+// workgroups of one launch costs tens of microseconds, so the chain of short
+// launches is the faster shape for a single persistent kernel.)
+#include "bucket_dev.h"
+#include "ffn_launch.h"
+#include "host.h"
+#include "launch.h"
+#include "route_dev.h"
+
+namespace moeblk {
+namespace {
+
+constexpr int kTopkThreads = 1024;
+
+// top-k of every token (wave w takes tokens w, w + 16, ...), then the
+// bucketing of the picks, in one workgroup
+__global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
+    const float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ rows,
+    int32_t* __restrict__ pick_pos, int32_t* __restrict__ active, int S, int E, int topk,
+    int renorm, int n_loc, int local_base, int R_max) {
+  __shared__ float sl[kTopkThreads / kWave][8];
+  __shared__ int se[kTopkThreads / kWave][8];
+  __shared__ BucketLds L;
+  const int wv = threadIdx.x >> 6;
+  for (int t = wv; t < S; t += kTopkThreads / kWave)
+    topk_token(logits, ids, w, E, topk, renorm, t, sl[wv], se[wv]);
+  __syncthreads();
+  bucket_block(ids, S, topk, n_loc, local_base, R_max, L, nullptr, true, counts, offsets, rows,
+               pick_pos, active);
+}
+
+}  // namespace
+}  // namespace moeblk
+
+using namespace moeblk;
+
+extern "C" size_t moe_forward_workspace_bytes(const moe_dims* dims) {
+  if (check_dims(dims)) return 0;
+  return ffn_layout(*dims).total;
+}
+
+extern "C" int moe_forward(const moe_dims* dims, const void* x, const float* w_router,
+                           const float* bias, const void* w13_packed, const void* w2_packed,
+                           const void* ws13_packed, const void* ws2_packed, const void* gamma,
+                           float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* rows, int32_t* pick_pos, int32_t* active,
+                           void* y, float* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const int rc = check_dims(dims);
+  if (rc) return rc;
+  const moe_dims& m = *dims;
+  MOE_REQUIRE(x && w_router && w13_packed && w2_packed && logits && topk_ids && topk_w && counts &&
+                  offsets && rows && pick_pos && active && y && out && workspace,
+              MOE_ERR_NULL);
+  MOE_REQUIRE(m.shared_I == 0 || (ws13_packed && ws2_packed), MOE_ERR_NULL);
+  MOE_REQUIRE(aligned16(x) && aligned16(w_router) && (!bias || aligned16(bias)) &&
+                  aligned16(w13_packed) && aligned16(w2_packed) &&
+                  (!ws13_packed || aligned16(ws13_packed)) && (!ws2_packed || aligned16(ws2_packed)) &&
+                  (!gamma || aligned16(gamma)) && aligned16(logits) && aligned16(topk_ids) &&
+                  aligned16(topk_w) && aligned16(counts) && aligned16(offsets) && aligned16(rows) &&
+                  aligned16(pick_pos) && aligned16(active) && aligned16(y) && aligned16(out) &&
+                  aligned16(workspace),
+              MOE_ERR_ALIGN);
+  MOE_REQUIRE(workspace_bytes >= moe_forward_workspace_bytes(dims), MOE_ERR_WORKSPACE);
+
+  launch_router_logits(m, x, w_router, bias, logits, stream);
+  hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits, topk_ids,
+                     topk_w, counts, offsets, rows, pick_pos, active, m.S, m.E, m.topk, m.renorm,
+                     m.n_local, m.local_base, r_max(m));
+  const int frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y,
+                             workspace, stream);
+  if (frc) return frc;
+  launch_combine(m, y, topk_w, pick_pos, gamma, out, stream);
+  return launch_status();
+}

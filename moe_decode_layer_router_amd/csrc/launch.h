@@ -1,0 +1,17 @@
+// launch.h -- enqueue functions of the steps (arguments already checked),
+// shared by the entry points.
+#pragma once
+
+#include "host.h"
+
+namespace moeblk {
+
+void launch_router_logits(const moe_dims& m, const void* x, const float* wr, const float* bias,
+                          float* logits, hipStream_t stream);
+void launch_topk(const moe_dims& m, const float* logits, int32_t* ids, float* w, hipStream_t stream);
+void launch_bucket(const moe_dims& m, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                   int32_t* rows, int32_t* pick_pos, int32_t* active, hipStream_t stream);
+void launch_combine(const moe_dims& m, const void* y, const float* w, const int32_t* pick_pos,
+                    const void* gamma, float* out, hipStream_t stream);
+
+}  // namespace moeblk

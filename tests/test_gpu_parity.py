@@ -87,6 +87,8 @@ EDGE = {
     "shared_S128": _tiny(S=128, E=16, n_local=4, topk=2, shared_I=256, d=256),
     "scales_wide": _tiny(S=8, e8m0_lo=100, e8m0_hi=150),
     "zipf": _tiny(S=48, E=64, n_local=8, local_base=8, topk=8, bias_kind="zipf", zipf_s=1.1),
+    "d_max16384": _tiny(S=4, d=16384, I=128),
+    "d7168_S33": _tiny(S=33, d=7168, I=128, E=32, n_local=8, topk=8),
 }
 
 
@@ -141,3 +143,66 @@ def test_full_workload(name, n_tok):
     inp = make_inputs(cfg, 0, gamma="random")
     g = run_gpu(inp)
     check_block(inp, g, tokens=_sample_tokens(g, cfg, n_tok), strict=True)
+
+
+# ------------------------------------------------------------ moe_forward
+
+FUSED = {
+    "tiny": get_config("tiny"),
+    "S13_ragged": _tiny(S=13),
+    "buckets_gt32": _tiny(S=64, E=8, n_local=8, topk=4),
+    "shared_S128": _tiny(S=128, E=16, n_local=4, topk=2, shared_I=256, d=256),
+    "d640_I256": _tiny(S=6, d=640, I=256, E=16, n_local=4, local_base=4, topk=3),
+    "d7168_S33": _tiny(S=33, d=7168, I=128, E=32, n_local=8, topk=8),
+    "no_local": _tiny(S=12, E=16, n_local=4, local_base=8, topk=2, bias_kind="local", beta=-50.0),
+}
+
+KEYS = ("logits", "ids", "w", "counts", "offsets", "rows", "pick_pos", "active", "out")
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_fused_equals_four_calls(name):
+    """moe_forward runs the same device code in the same order as the four
+    calls: every output is bit-identical, and both match the oracle."""
+    inp = make_inputs(FUSED[name], 11, gamma="random")
+    g4 = run_gpu(inp)
+    g1 = run_gpu(inp, g4["blk"], fused=True)
+    for k in KEYS:
+        assert np.array_equal(g1[k], g4[k]), k
+    R = g4["blk"].dims.r_max
+    n = int(g4["offsets"][-1])
+    assert np.array_equal(g1["y"][:n], g4["y"][:n])
+    if FUSED[name].shared_I:
+        assert np.array_equal(g1["y"][R:], g4["y"][R:])
+    check_block(inp, g1, strict=(name in ("tiny", "no_local")))
+
+
+@pytest.mark.parametrize("name,n_tok", [("s8_uniform", 8), ("s64_zipf", 3), ("s128_shared", 2)])
+def test_fused_full_workload(name, n_tok):
+    cfg = get_config(name)
+    inp = make_inputs(cfg, 0, gamma="random")
+    g1 = run_gpu(inp, fused=True)
+    check_block(inp, g1, tokens=_sample_tokens(g1, cfg, n_tok), strict=True)
+    g4 = run_gpu(inp, g1["blk"])
+    for k in KEYS:
+        assert np.array_equal(g1[k], g4[k]), k
+
+
+def test_fused_repeated_calls_agree():
+    """The FFN counters return to zero within every launch: back-to-back calls
+    agree, through both entry points."""
+    inp = make_inputs(_tiny(S=64, E=8, n_local=8, topk=4), 3)
+    from moe_decode_layer_router_amd.block import MoeBlock
+
+    blk = MoeBlock(inp)
+    outs = []
+    for i in range(6):
+        if i % 2:
+            blk.forward()
+        else:
+            blk.step()
+        torch.cuda.synchronize()
+        assert blk.forward_error() == 0 and blk.ffn_error() == 0
+        outs.append(to_np(blk.out))
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
