@@ -3,7 +3,7 @@
 
 A step is one pass of the whole block -- route, bucket, expert FFN, combine --
 over one batch of S token rows, all inputs resident in HBM. It is timed as the
-library's single-launch entry point moe_forward (the headline `value`) and, for
+library's one-call entry point moe_forward (the headline `value`) and, for
 comparison, as the four calls moe_route -> moe_bucket -> moe_expert_ffn ->
 moe_combine. The default workload is S = 8, d = 4096, 256 experts (32 local),
 I = 2048, top-8 uniform routing ("s8_uniform").
@@ -14,11 +14,12 @@ every weight set with R x (active bytes) >= 512 MiB and rotates through them
 step by step; every step then streams its weights from HBM, as a decode step
 does between the other layers' weights.
 
-Output: one JSON line (see the fields below). ``roofline`` covers the
-dominant kernel, the moe_forward launch (the only kernel of a step), timed with
-HIP events around each launch on its stream in a separate timed pass; its
-``traffic`` comes from the committed rocprofv3 counter summary when that summary
-was taken on the current kernel sources, else null.
+Output: one JSON line (see the fields below). ``roofline`` covers the dominant
+work, the expert FFN (one moe_expert_ffn call: the gate_up + SwiGLU kernel and
+the down kernel, about 95% of a step's bytes), timed with HIP events around
+each call on the stream its kernels run on, in a separate timed pass; its
+``traffic`` comes from the committed rocprofv3 counter summary when that
+summary was taken on the current kernel sources, else null.
 ``cpu_baseline`` times the CPU oracle on the same workload.
 """
 
@@ -39,8 +40,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 LLC_BYTES = 256 * 2**20  # MI355X Infinity Cache
 KERNEL_SOURCES = [
-    "moe_decode_layer_router_amd/csrc/" + f
-    for f in ("forward.hip", "ffn_dev.h", "route_dev.h", "bucket_dev.h", "combine_dev.h", "common.h")
+    "moe_decode_layer_router_amd/csrc/" + f for f in ("ffn.hip", "ffn_dev.h", "ffn_launch.h", "common.h")
 ]
 
 
@@ -53,9 +53,9 @@ def kernel_source_sha() -> str:
 
 
 def committed_traffic(workload: str):
-    """HBM bytes one moe_forward launch moves, from profiles/, if taken on the
-    current kernel sources (else None)."""
-    p = os.path.join(ROOT, "profiles", f"moe_forward_{workload}_traffic.md")
+    """HBM bytes one moe_expert_ffn call moves (both kernels), from profiles/,
+    if taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", f"expert_ffn_{workload}_traffic.md")
     if not os.path.exists(p):
         return None
     txt = open(p).read()
@@ -133,7 +133,7 @@ def main() -> int:
     b_router = cfg.E * cfg.d * 4
     b_shared = 3 * cfg.shared_I * cfg.d * 2
     b_step_w = b_mx + b_router + b_shared
-    copies = args.copies or max(1, math.ceil(2 * LLC_BYTES / max(b_step_w, 1)))
+    copies = args.copies or max(1, math.ceil(2 * LLC_BYTES / max(b_mx + b_shared, 1)))
     blk.add_weight_copies(copies - 1)
     torch.cuda.synchronize()
 
@@ -161,31 +161,48 @@ def main() -> int:
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / K
 
-    # timed pass 1: whole steps, one launch each (the headline)
+    def per_call(fn, n):
+        """Event pairs around each of n calls on the current stream -> ms each."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(min(args.warmup, n)):
+            fn(i % copies)
+        torch.cuda.synchronize()
+        for i in range(n):
+            evs[i][0].record()
+            fn(i % copies)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
+
+    # timed pass 1: whole steps through moe_forward (the headline)
     ms = timed(blk.forward)
     # timed pass 2: whole steps as the four calls
     ms4 = timed(blk.step)
-    # timed pass 3: each launch bracketed by events on its stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        evs[i][0].record()
-        blk.forward(i % copies)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / K
-    assert blk.forward_error() == 0, "a wait in the fused launch hit its bound"
+    # pass 3: each step bracketed by its own events (median and spread)
+    st = per_call(blk.forward, K)
+    # pass 4: the same weight copy every step (warm last-level cache, labelled)
+    ms_warm = timed(lambda _i: blk.forward(0))
+    # pass 5: each expert-FFN call bracketed by events on its stream; routing
+    # and buckets are those of the step (identical for every weight copy)
+    blk.forward(0)
+    ffn = per_call(blk.expert_ffn, K)
+    ffn_ms = sum(ffn) / len(ffn)
 
-    # algorithmic bytes of one launch: the router weights, the active experts'
-    # MXFP4 weights, the shared expert's bf16 weights, x read, h written and
-    # read, y written and read, logits written and read, out written
-    b_act = cfg.S * cfg.d * 2 + picks * cfg.I * 2 * 2 + picks * cfg.d * 2 * 2
-    b_act += cfg.S * cfg.E * 4 * 2 + cfg.S * cfg.d * 4
+    # algorithmic bytes of one expert-FFN call: the active experts' MXFP4
+    # weights, the shared expert's bf16 weights, x read, SwiGLU rows written
+    # and read, y written
+    b_ffn = b_mx + b_shared + cfg.S * cfg.d * 2 + picks * cfg.I * 2 * 2 + picks * cfg.d * 2
     if cfg.shared_I:
-        b_act += cfg.S * cfg.shared_I * 2 * 2 + cfg.S * cfg.d * 2 * 2
-    launch_bytes = b_step_w + b_act
-    achieved = launch_bytes / (kern_ms * 1e-3) / 1e9
+        b_ffn += cfg.S * cfg.shared_I * 2 * 2 + cfg.S * cfg.d * 2
+    achieved = b_ffn / (ffn_ms * 1e-3) / 1e9
     traffic = committed_traffic(cfg.name)
+
+    # read bandwidth of a torch reduction over 1 GiB (context only: not a
+    # tuned streaming kernel)
+    big = torch.ones(2**28, dtype=torch.float32, device="cuda:0")
+    rd = per_call(lambda _i: big.sum(), 20)
+    read_gbps = big.numel() * 4 / (rd[len(rd) // 2] * 1e-3) / 1e9
+    del big
 
     tok_s = cfg.S / (ms * 1e-3)
     line = {
@@ -217,16 +234,21 @@ def main() -> int:
         "mxfp4_weight_gbps": round(b_mx / (ms * 1e-3) / 1e9, 1),
         "all_weight_pct_hbm_peak": round(100 * b_step_w / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "four_call_ms_per_step": round(ms4, 5),
+        "step_ms_median": round(st[len(st) // 2], 5),
+        "step_ms_p10": round(st[len(st) // 10], 5),
+        "step_ms_p90": round(st[(9 * len(st)) // 10], 5),
+        "warm_llc_ms_per_step": round(ms_warm, 5),
+        "torch_sum_read_gbps": round(read_gbps, 1),
         "roofline": {
-            "kernel": "moe_forward_kernel (the whole step in one launch)",
+            "kernel": "moe_expert_ffn (gate_up_kernel + down_kernel)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": launch_bytes,
-            "avg_ms": round(kern_ms, 5),
+            "algorithmic_bytes": b_ffn,
+            "avg_ms": round(ffn_ms, 5),
         },
         "cpu_baseline": None,
     }

@@ -1,5 +1,5 @@
-// ffn_launch.h -- the expert-FFN launch shared by moe_expert_ffn and
-// moe_forward: its argument block and workspace layout.
+// ffn_launch.h -- the expert-FFN launches shared by moe_expert_ffn and
+// moe_forward: their argument block and workspace layout.
 #pragma once
 
 #include "common.h"
@@ -21,14 +21,11 @@ struct FfnArgs {
   uint16_t* h;     // workspace: SwiGLU rows of the bucket rows [R_max][I]
   uint16_t* hs;    // workspace: the shared expert's SwiGLU rows [S][Is]
   uint16_t* y;     // [R_max (+ S)][d]
-  int32_t* prod;   // workspace: gate_up tasks done, a work item
-  int32_t* cons;   // workspace: down tasks past their wait, a work item
-  int32_t* error;  // workspace: nonzero if a wait hit its bound
   int S, d, I, Is, n_loc, R_max, max_work;
 };
 
 struct FfnLayout {
-  size_t h, hs, prod, cons, error, total;
+  size_t h, hs, total;
   int max_work;
 };
 

@@ -1,16 +1,16 @@
-// forward.hip -- moe_forward: the whole block as four launches on one stream.
+// forward.hip -- moe_forward: the whole block as five launches on one stream.
 //
 //   1  router logits (one workgroup an expert row)
 //   2  top-k of every token and the bucketing, in one workgroup
-//   3  the expert FFNs (gate_up, SwiGLU, down, shared expert) in one launch
+//   3  the expert FFNs: gate_up + SwiGLU, then down (shared expert included)
 //   4  per-pick RMSNorm and the weighted sum (one workgroup a token)
 //
 // The outputs are those of moe_route, moe_bucket, moe_expert_ffn and
 // moe_combine, bit for bit: the same device code runs in the same order.
-// Steps 2 and 3 each replace two launches of the four-call path. (Measured on
-// MI355X: a launch costs about 2.5 us, while a grid-wide barrier across all
-// workgroups of one launch costs tens of microseconds, so the chain of short
-// launches is the faster shape for a single persistent kernel.)
+// Step 2 replaces two launches of the four-call path. (Measured on MI355X: a
+// dependent launch costs about 2.5 us, while a grid-wide barrier inside one
+// launch costs tens of microseconds, so a chain of short launches is faster
+// than one persistent kernel.)
 #include "bucket_dev.h"
 #include "ffn_launch.h"
 #include "host.h"

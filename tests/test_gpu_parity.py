@@ -189,12 +189,14 @@ def test_fused_full_workload(name, n_tok):
 
 
 def test_fused_repeated_calls_agree():
-    """The FFN counters return to zero within every launch: back-to-back calls
-    agree, through both entry points."""
+    """Back-to-back calls through both entry points agree, starting from
+    workspaces filled with garbage (no call depends on their contents)."""
     inp = make_inputs(_tiny(S=64, E=8, n_local=8, topk=4), 3)
     from moe_decode_layer_router_amd.block import MoeBlock
 
     blk = MoeBlock(inp)
+    blk.ws.fill_(0xA5)
+    blk.fws.fill_(0x5A)
     outs = []
     for i in range(6):
         if i % 2:
@@ -202,7 +204,6 @@ def test_fused_repeated_calls_agree():
         else:
             blk.step()
         torch.cuda.synchronize()
-        assert blk.forward_error() == 0 and blk.ffn_error() == 0
         outs.append(to_np(blk.out))
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
