@@ -1,5 +1,5 @@
 // bucket_dev.h -- the local experts' picks grouped by expert, as a
-// workgroup-level device function (moe_bucket kernel and the fused kernel).
+// workgroup-level device function (moe_bucket and moe_forward).
 //
 // Muse Spark K3 page, stage "route": from every token's top-8, the picks of
 // this rank's experts; function "dn_loads": the table etab[u] of the active

@@ -1,5 +1,5 @@
 // combine_dev.h -- per-pick RMSNorm and the routing-weighted sum of one token,
-// as a workgroup-level device function (moe_combine kernel, fused kernel).
+// as a workgroup-level device function (moe_combine and moe_forward).
 //
 // Muse Spark K3 page, stage "E": each pick's expert output is normalised (the
 // post-expert norm) and the picks are summed with their routing weights into

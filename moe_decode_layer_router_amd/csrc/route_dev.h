@@ -1,5 +1,5 @@
 // route_dev.h -- router logits (fp32) and sigmoid top-k as device functions,
-// used by the moe_route kernels and by the fused forward kernel.
+// used by the moe_route kernels and by moe_forward.
 //
 // Muse Spark K3 page, stage "A": router logits in fp32; stage "route": every
 // token's top-8, identical wherever computed. K5 page, HA routing tail: top-8
