@@ -187,6 +187,7 @@ def main() -> int:
     blk.forward(0)
     ffn = per_call(blk.expert_ffn, K)
     ffn_ms = sum(ffn) / len(ffn)
+    assert blk.forward_error() == 0 and blk.ffn_error() == 0, "a wait in an FFN launch hit its bound"
 
     # algorithmic bytes of one expert-FFN call: the active experts' MXFP4
     # weights, the shared expert's bf16 weights, x read, SwiGLU rows written

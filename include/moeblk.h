@@ -154,8 +154,9 @@ int moe_bucket(const moe_dims* dims, const int32_t* topk_ids, int32_t* counts, i
                int32_t* rows, int32_t* pick_pos, int32_t* active, hipStream_t stream);
 
 /* Bytes of scratch moe_expert_ffn needs: the SwiGLU rows of every bucket row
- * (R_max x I bf16) and, with a shared expert, those of every token (S x
- * shared_I bf16). 0 if `dims` is invalid. */
+ * (R_max x I bf16), with a shared expert those of every token (S x shared_I
+ * bf16), then counters that order the down GEMMs after the gate_up GEMMs
+ * inside one launch, and an error word. 0 if `dims` is invalid. */
 size_t moe_ffn_workspace_bytes(const moe_dims* dims);
 
 /* The expert FFNs (K3 page stages "C, D"): for every bucket row r of local
@@ -172,11 +173,19 @@ size_t moe_ffn_workspace_bytes(const moe_dims* dims);
  *   ws13_packed, ws2_packed: moe_pack_bf16 outputs, or NULL when shared_I == 0;
  *   y          [R_max + (shared_I ? S : 0), d] bf16, written for rows < offsets[n_local]
  *              and the shared rows; other rows are left as they were;
- *   workspace  device scratch of at least moe_ffn_workspace_bytes(dims), any
- *              contents; undefined after the call. Calls sharing a workspace
- *              must not overlap.
- * Two launches: gate_up + SwiGLU, then down (the down GEMM of an expert needs
- * all of its SwiGLU rows, K3 page stages "C, D"). */
+ *   workspace  device scratch of at least moe_ffn_workspace_bytes(dims). It must
+ *              be zero-filled once before its first use; every call leaves its
+ *              counters at zero again (the rest is undefined afterwards).
+ *              Calls sharing a workspace must not overlap. The 32-bit word at
+ *              byte offset moe_ffn_workspace_bytes(dims) - 256 is set nonzero by
+ *              a call in which a wait hit its time bound (a correct run never
+ *              does; that call's outputs are undefined and the workspace must
+ *              be zero-filled again).
+ * The down GEMM of an expert needs all of its SwiGLU rows (K3 page, stages
+ * "C, D"). For S <= 16 without a shared expert the FFNs are one launch: a down
+ * task issues its first weight loads, then waits on a counter of its expert's
+ * finished gate_up tasks. Otherwise they are two launches, gate_up + SwiGLU
+ * then down. */
 int moe_expert_ffn(const moe_dims* dims, const void* x, const void* w13_packed,
                    const void* w2_packed, const int32_t* counts, const int32_t* offsets,
                    const int32_t* rows, const int32_t* active, const void* ws13_packed,
@@ -203,10 +212,11 @@ int moe_combine(const moe_dims* dims, const void* y, const float* topk_w, const 
 size_t moe_forward_workspace_bytes(const moe_dims* dims);
 
 /* The whole block -- the work of moe_route, moe_bucket, moe_expert_ffn and
- * moe_combine -- in five launches instead of six: top-k and bucketing share
- * one workgroup. Arguments and outputs are those of the four calls, with
+ * moe_combine -- with one launch fewer than the four calls: top-k and
+ * bucketing share one workgroup. Arguments and outputs are those of the four calls, with
  * identical values (the same device code runs in the same order). `workspace`
- * follows the moe_expert_ffn rules (any contents, calls sharing it must not
+ * follows the moe_expert_ffn rules (zero-filled once before first use, error
+ * word at byte moe_forward_workspace_bytes - 256, calls sharing it must not
  * overlap). */
 int moe_forward(const moe_dims* dims, const void* x, const float* w_router, const float* bias,
                 const void* w13_packed, const void* w2_packed, const void* ws13_packed,

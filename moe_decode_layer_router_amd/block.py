@@ -96,9 +96,9 @@ class MoeBlock:
         self.active = torch.empty(n + 1, **i32)
         self.y = torch.zeros((R + (S if cfg.shared_I else 0), d), dtype=torch.bfloat16, device=dv)
         self.out = torch.empty((S, d), dtype=torch.float32, device=dv)
-        # workspaces (the calls need no particular contents)
-        self.ws = torch.empty(max(moe_ffn_workspace_bytes(self.dims), 16), dtype=torch.uint8, device=dv)
-        self.fws = torch.empty(max(moe_forward_workspace_bytes(self.dims), 16), dtype=torch.uint8, device=dv)
+        # workspaces: zero-filled once (the calls keep their counters at zero)
+        self.ws = torch.zeros(max(moe_ffn_workspace_bytes(self.dims), 16), dtype=torch.uint8, device=dv)
+        self.fws = torch.zeros(max(moe_forward_workspace_bytes(self.dims), 16), dtype=torch.uint8, device=dv)
 
     def add_weight_copies(self, n: int) -> None:
         """Append n device copies of the first weight set (same bytes)."""
@@ -138,3 +138,16 @@ class MoeBlock:
             self.logits, self.ids, self.w, self.counts, self.offsets, self.rows, self.pick_pos, self.active,
             self.y, self.out, self.fws,
         )
+
+    @staticmethod
+    def _error_word(ws) -> int:
+        n = ws.numel()
+        return int(ws[n - 256 : n - 252].view(torch.int32).item())
+
+    def ffn_error(self) -> int:
+        """moe_expert_ffn's wait-bound error word (0: no wait hit its bound)."""
+        return self._error_word(self.ws)
+
+    def forward_error(self) -> int:
+        """moe_forward's wait-bound error word (0: no wait hit its bound)."""
+        return self._error_word(self.fws)

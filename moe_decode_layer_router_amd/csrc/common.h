@@ -92,6 +92,9 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// cache-policy operand of the buffer intrinsics: sc1 = device-scope coherent
+constexpr int kCpolSc1 = 16;
+
 template <typename T>
 __device__ __forceinline__ T ld_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));

@@ -1,16 +1,24 @@
-// ffn.hip -- moe_expert_ffn: the expert FFNs of one step as two launches,
-// gate_up + SwiGLU, then down (tasks in ffn_dev.h).
+// ffn.hip -- moe_expert_ffn: the expert FFNs of one step (tasks in ffn_dev.h).
 //
 // Muse Spark K3 page, stages "C, D": down needs every SwiGLU row of its expert,
-// a dependency across all workgroups of the gate_up stage. Here the kernel
-// boundary carries it. (Measured on MI355X: a dependent launch costs about
-// 2.5 us; a barrier across a resident grid, or per-item counters polled by
-// waiting workgroups, cost more than that at these sizes.)
+// a dependency across all workgroups of the gate_up stage. Two shapes:
 //
-// Grid of each launch: the shared expert's tasks first, then the routed work
-// items in order (item-major, row block minor), then workgroups past the last
-// item, which leave at once. The host does not know the bucket sizes, so the
-// grid covers the largest possible number of items.
+// * S <= 16 without a shared expert: ONE launch. Workgroup ids run over the
+//   gate_up tasks, then the down tasks (item-major, row block minor), then
+//   workgroups past the last item, which leave at once. Every workgroup reads
+//   the 32 bucket counts first, so the ids of real tasks are dense. A gate_up
+//   task writes its SwiGLU rows through to the coherence point (sc1) and counts
+//   itself in prod[item] once its stores are done; the last one of the item
+//   sets a ready flag for each of the item's down tasks. A down task issues
+//   its first weight loads, then waits for its flag, then reads the SwiGLU rows
+//   with coherent loads: its weights stream while gate_up finishes. At these
+//   sizes every task of the launch fits on the device at once.
+// * otherwise: two launches, gate_up + SwiGLU then down; the kernel boundary
+//   carries the dependency. Grid of each: the shared expert's tasks first,
+//   then the routed items, then workgroups past the last item.
+//
+// The host does not know the bucket sizes, so a grid covers the largest
+// possible number of items.
 #include "ffn_dev.h"
 #include "ffn_launch.h"
 #include "host.h"
@@ -18,6 +26,82 @@
 namespace moeblk {
 
 namespace {
+
+constexpr long long kWaitCycles = 1ll << 31;  // wait bound, about a second
+
+// thread 0 waits until its flag is set (bounded), then clears it for the next
+// call. The SwiGLU rows the flag covers are then read with coherent loads, so
+// no cache invalidation is needed (a device-scope acquire fence would
+// invalidate this XCD's whole L2). Every down task polls its own 128-byte line:
+// hundreds of workgroups polling one line would load a single memory channel.
+struct WaitFlag {
+  int32_t* flag;
+  int32_t* error;
+  __device__ void operator()() const {
+    if (threadIdx.x == 0) {
+      const long long t0 = clock64();
+      while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        __builtin_amdgcn_s_sleep(8);
+        if (clock64() - t0 > kWaitCycles) {
+          __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+};
+
+// A gate_up task of a work item is done. Its SwiGLU rows were written through
+// (sc1 stores): once every thread has seen its own stores complete, one count
+// publishes them. (A device-scope release fence would write back this XCD's
+// whole L2.) The task that brings the count to n resets it and sets the ready
+// flag of each of the item's nd down tasks.
+__device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int nd) {
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are done
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+  __syncthreads();
+  if (!last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = threadIdx.x; i < nd; i += blockDim.x)
+    __hip_atomic_store(&flags[i * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the single launch (S <= 16: one group of 16 rows an item, no shared expert);
+// PG / PD: chunks in flight a wave in gate_up / down tasks
+template <int PG, int PD>
+__global__ __launch_bounds__(kSplit * kWave, 4) void ffn_single_kernel(FfnArgs a) {
+  __shared__ f32x4_t red[kSplit][1][4][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
+  const int n_work = count_work<1>(cnt);
+  const int RB13 = 2 * a.I / kRowsPerBlock, NC13 = a.d / kChunkK;
+  const int RB2 = a.d / kRowsPerBlock, NC2 = a.I / kChunkK;
+  int t = blockIdx.x;
+  int el, row0, ntok;
+  if (t < n_work * RB13) {
+    const int wi = t / RB13, rb = t - wi * RB13;
+    find_task<1>(cnt, wi, el, row0, ntok);
+    const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB13 + rb) * NC13 * kMxTileBytes;
+    const int32_t* rows = a.rows;
+    ffn_task<true, 1, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
+                                      [rows](int r) { return rows[r]; }, NoWait{}, red);
+    publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
+    return;
+  }
+  t -= n_work * RB13;
+  if (t >= n_work * RB2) return;
+  const int wi = t / RB2, rb = t - wi * RB2;
+  find_task<1>(cnt, wi, el, row0, ntok);
+  const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB2 + rb) * NC2 * kMxTileBytes;
+  ffn_task<true, 1, PD, false, true>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d,
+                                     [](int r) { return r; }, WaitFlag{&a.ready[t * kCtlStride], a.error},
+                                     red);
+}
 
 template <int TTG, int P, bool kShared>
 __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
@@ -32,8 +116,8 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
       const int grp = t / RBs, rb = t - grp * RBs;
       const int row0 = grp * GS, ntok = min(GS, a.S - row0);
       const uint8_t* tiles = a.ws13 + static_cast<size_t>(rb) * NC * kBfTileBytes;
-      ffn_task<false, kSharedTTG, kSharedP, true>(
-          tiles, NC, a.x, a.d, row0, ntok, rb, a.hs, a.Is, [](int r) { return r; },
+      ffn_task<false, kSharedTTG, kSharedP, true, false>(
+          tiles, NC, a.x, a.d, row0, ntok, rb, a.hs, a.Is, [](int r) { return r; }, NoWait{},
           reinterpret_cast<f32x4_t(*)[kSharedTTG][4][kWave]>(&red[0][0][0][0]));
       return;
     }
@@ -47,9 +131,9 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
   if (!find_task<TTG>(cnt, wi, el, row0, ntok)) return;
   const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
   const int32_t* rows = a.rows;
-  ffn_task<true, TTG, P, true>(tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I,
-                               [rows](int r) { return rows[r]; },
-                               reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
+  ffn_task<true, TTG, P, true, false>(tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I,
+                                      [rows](int r) { return rows[r]; }, NoWait{},
+                                      reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }
 
 template <int TTG, int P, bool kShared>
@@ -66,9 +150,9 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
       const int grp = t / RB, rb = t - grp * RB;
       const int row0 = grp * GS, ntok = min(GS, a.S - row0);
       const uint8_t* tiles = a.ws2 + static_cast<size_t>(rb) * NCs * kBfTileBytes;
-      ffn_task<false, kSharedTTG, kSharedP, false>(
+      ffn_task<false, kSharedTTG, kSharedP, false, false>(
           tiles, NCs, a.hs, a.Is, row0, ntok, rb, a.y + static_cast<size_t>(a.R_max) * a.d, a.d,
-          same, reinterpret_cast<f32x4_t(*)[kSharedTTG][4][kWave]>(&red[0][0][0][0]));
+          same, NoWait{}, reinterpret_cast<f32x4_t(*)[kSharedTTG][4][kWave]>(&red[0][0][0][0]));
       return;
     }
     t -= n_sg * RB;
@@ -80,8 +164,8 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
   int el, row0, ntok;
   if (!find_task<TTG>(cnt, wi, el, row0, ntok)) return;
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
-  ffn_task<true, TTG, P, false>(tiles, NC, a.h, a.I, row0, ntok, rb, a.y, a.d, same,
-                                reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
+  ffn_task<true, TTG, P, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb, a.y, a.d, same,
+                                       NoWait{}, reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }
 
 // PG / PD: chunks in flight a wave in gate_up / down
@@ -96,15 +180,20 @@ void launch_pair(const FfnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((down_kernel<TTG, PD, kShared>), dim3(g2), dim3(kSplit * kWave), 0, stream, a);
 }
 
+bool single_launch(const moe_dims& m) { return ffn_group(m) == 16 && m.shared_I == 0; }
+
 }  // namespace
 
 FfnLayout ffn_layout(const moe_dims& m) {
   const int R = r_max(m);
   FfnLayout l;
-  l.max_work = max_work(R, m.n_local, ffn_group(m));
+  l.max_work = max_work(m);
   l.h = 0;
   l.hs = round_up(static_cast<size_t>(R) * m.I * 2, 256);
-  l.total = l.hs + round_up(static_cast<size_t>(m.S) * m.shared_I * 2, 256);
+  l.prod = l.hs + round_up(static_cast<size_t>(m.S) * m.shared_I * 2, 256);
+  l.ready = l.prod + static_cast<size_t>(l.max_work) * kCtlStride * 4;
+  l.error = l.ready + static_cast<size_t>(l.max_work) * (m.d / kRowsPerBlock) * kCtlStride * 4;
+  l.total = l.error + 256;
   return l;
 }
 
@@ -123,6 +212,9 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   a.counts = counts;
   a.h = reinterpret_cast<uint16_t*>(ws + l.h);
   a.hs = reinterpret_cast<uint16_t*>(ws + l.hs);
+  a.prod = reinterpret_cast<int32_t*>(ws + l.prod);
+  a.ready = reinterpret_cast<int32_t*>(ws + l.ready);
+  a.error = reinterpret_cast<int32_t*>(ws + l.error);
   a.y = static_cast<uint16_t*>(y);
   a.S = m.S;
   a.d = m.d;
@@ -132,7 +224,10 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   a.R_max = r_max(m);
   a.max_work = l.max_work;
   const bool big = ffn_group(m) > 16;
-  if (m.shared_I) big ? launch_pair<2, 2, 2, true>(a, stream) : launch_pair<1, 2, 4, true>(a, stream);
+  if (single_launch(m)) {
+    const int grid = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
+    hipLaunchKernelGGL((ffn_single_kernel<2, 2>), dim3(grid), dim3(kSplit * kWave), 0, stream, a);
+  } else if (m.shared_I) big ? launch_pair<2, 2, 2, true>(a, stream) : launch_pair<1, 2, 4, true>(a, stream);
   else big ? launch_pair<2, 2, 2, false>(a, stream) : launch_pair<1, 2, 4, false>(a, stream);
   return launch_status();
 }

@@ -1,5 +1,5 @@
 // ffn_dev.h -- one task of the expert GEMMs (gate_up + SwiGLU, or down) as a
-// workgroup-level device function, used by the two moe_expert_ffn kernels.
+// workgroup-level device function, used by the moe_expert_ffn kernels.
 //
 // Muse Spark K3 page, stages "C, D": gate_up and down of the local experts with
 // MXFP4 weights decoded in registers and fed to bf16 MFMA; functions "mx_chunk"
@@ -86,22 +86,40 @@ struct BfChunk {
 
 // Activation (B) rows of a task. Loads are unconditional (every token tile,
 // clamped chunk indices): the waitcnt insertion then sees one fixed issue order
-// and keeps the ring in flight.
-template <int TTG>
+// and keeps the ring in flight. With kCoh the loads carry the device-scope
+// coherence bit (sc1): rows written earlier in the same launch by another XCD
+// are read from the coherence point, not from a stale line of this XCD's L2.
+template <int TTG, bool kCoh>
 struct BRows {
-  const uint16_t* bp[TTG];  // this lane's row pointers (+ its K group)
+  const uint16_t* bp[TTG];      // !kCoh: this lane's row pointers (+ its K group)
+  __amdgpu_buffer_rsrc_t rsrc;  // kCoh: buffer over the B rows
+  uint32_t boff[TTG];           // kCoh: this lane's byte offsets
 
   __device__ __forceinline__ void init(const uint16_t* bsrc, int K, const int (&src)[TTG], int g) {
+    if constexpr (kCoh) {
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(bsrc), 0, 0x7fffffff,
+                                               0x00020000);
 #pragma unroll
-    for (int tt = 0; tt < TTG; ++tt) bp[tt] = bsrc + static_cast<size_t>(src[tt]) * K + 32 * g;
+      for (int tt = 0; tt < TTG; ++tt) boff[tt] = (static_cast<uint32_t>(src[tt]) * K + 32 * g) * 2u;
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < TTG; ++tt) bp[tt] = bsrc + static_cast<size_t>(src[tt]) * K + 32 * g;
+    }
   }
 
   __device__ __forceinline__ void load(u32x4_t (&b)[TTG][4], int c) const {
 #pragma unroll
     for (int tt = 0; tt < TTG; ++tt) {
-      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(bp[tt] + c * kChunkK);
+      if constexpr (kCoh) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[tt][q] = p[q];
+        for (int q = 0; q < 4; ++q)
+          b[tt][q] = __builtin_amdgcn_raw_buffer_load_b128(
+              rsrc, boff[tt] + static_cast<uint32_t>(c * kChunkK + 8 * q) * 2u, 0, kCpolSc1);
+      } else {
+        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(bp[tt] + c * kChunkK);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[tt][q] = p[q];
+      }
     }
   }
 };
@@ -157,15 +175,23 @@ __device__ __forceinline__ void compute_chunk(const BfChunk<TTG>& ch, f32x4_t (&
     }
 }
 
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
 // Workgroup-level (4 waves). tiles: the packed tiles of (expert, row block rb);
 // B rows: src_of(r) for bucket rows r = row0 .. row0 + ntok - 1 (row length K;
 // gate_up: token rows of x; down: SwiGLU rows); out: output rows indexed by
-// bucket row (row length out_ld); red: LDS.
-template <bool kMx, int TTG, int P, bool kGateUp, class SrcOf>
+// bucket row (row length out_ld); before_b() runs after the weight prefetch and
+// before the first activation load; red: LDS. kCoh: the SwiGLU rows pass
+// between workgroups of one launch (gate_up writes them through to the
+// coherence point, down reads them from there).
+template <bool kMx, int TTG, int P, bool kGateUp, bool kCoh, class SrcOf, class BeforeB>
 __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int NC,
                                          const uint16_t* __restrict__ bsrc, int K, int row0,
                                          int ntok, int rb, uint16_t* __restrict__ out, int out_ld,
-                                         SrcOf src_of, f32x4_t (*red)[TTG][4][kWave]) {
+                                         SrcOf src_of, BeforeB before_b,
+                                         f32x4_t (*red)[TTG][4][kWave]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
   const int g = lane >> 4;
@@ -187,7 +213,9 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
 #pragma unroll
   for (int i = 0; i < P; ++i) load_w<TTG>(ring[i], wlane, slane, min(w + kSplit * i, NC - 1));
 
-  BRows<TTG> bp;
+  before_b();
+
+  BRows<TTG, kCoh && !kGateUp> bp;
   bp.init(bsrc, K, src, g);
 #pragma unroll
   for (int i = 0; i < P; ++i) bp.load(ring[i].b, min(w + kSplit * i, NC - 1));
@@ -246,20 +274,16 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
       const float g0 = round_bf16(s[0]), g1 = round_bf16(s[1]);
       const float u0 = round_bf16(s[2]), u1 = round_bf16(s[3]);
       const int i0 = 32 * rb + 8 * r + 2 * g;
-      *reinterpret_cast<uint32_t*>(orow + i0) =
-          swiglu_bf16_bits(g0, u0) | (swiglu_bf16_bits(g1, u1) << 16);
+      const uint32_t hv = swiglu_bf16_bits(g0, u0) | (swiglu_bf16_bits(g1, u1) << 16);
+      uint32_t* hp = reinterpret_cast<uint32_t*>(orow + i0);
+      if constexpr (kCoh) __hip_atomic_store(hp, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *hp = hv;
     } else {
       const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
       *reinterpret_cast<u32x2_t*>(orow + n0) =
           u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
     }
   }
-}
-
-// upper bound of the work items: sum over experts of ceil(count / G)
-inline int max_work(int R_max, int n_loc, int G) {
-  const int experts = n_loc < R_max ? n_loc : R_max;
-  return experts + R_max / G;
 }
 
 }  // namespace moeblk

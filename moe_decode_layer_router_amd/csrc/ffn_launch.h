@@ -21,17 +21,35 @@ struct FfnArgs {
   uint16_t* h;     // workspace: SwiGLU rows of the bucket rows [R_max][I]
   uint16_t* hs;    // workspace: the shared expert's SwiGLU rows [S][Is]
   uint16_t* y;     // [R_max (+ S)][d]
+  int32_t* prod;   // workspace: gate_up tasks done, a work item (single launch)
+  int32_t* ready;  // workspace: a flag a down task: its item's SwiGLU rows are written
+  int32_t* error;  // workspace: nonzero if a wait hit its bound
   int S, d, I, Is, n_loc, R_max, max_work;
 };
 
+// ints between two counters or flags (one 128-byte line each)
+constexpr int kCtlStride = 32;
+
+// workspace: SwiGLU rows h [R_max][I] and hs [S][Is] (bf16), then the
+// counters prod (max_work lines), the ready flags (max_work * d / 64 lines)
+// and the error word; these must start at zero and are left at zero
 struct FfnLayout {
-  size_t h, hs, total;
+  size_t h, hs, prod, ready, error, total;
   int max_work;
 };
 
 // bucket rows a routed work item holds: 16 while no expert can get more than
 // 16 picks (S <= 16), else 32
 inline int ffn_group(const moe_dims& m) { return m.S > 16 ? 32 : 16; }
+
+// upper bound of the work items, sum over experts of ceil(count / G): with
+// S <= G every expert with picks has one item
+inline int max_work(const moe_dims& m) {
+  const int R = r_max(m);
+  const int G = ffn_group(m);
+  const int experts = m.n_local < R ? m.n_local : R;
+  return m.S <= G ? experts : experts + R / G;
+}
 
 FfnLayout ffn_layout(const moe_dims& m);
 

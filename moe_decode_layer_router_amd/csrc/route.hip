@@ -6,15 +6,14 @@
 namespace moeblk {
 namespace {
 
+// one workgroup an expert row
 template <int NW>
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const float* __restrict__ wr,
-                                                            const float* __restrict__ bias,
-                                                            float* __restrict__ logits, int S,
-                                                            int d, int E) {
-  __shared__ float red[4][kTok];
-  // d > 8192 (NW = 16): one tile buffer, for the register budget
-  router_row<NW, (NW <= 8)>(x, wr, bias, logits, S, d, E, blockIdx.x, red);
+__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    float* __restrict__ logits, int S, int d, int E) {
+  __shared__ float red[kRouteWaves][kTok];
+  // NW = 4 (d > 8192): one tile buffer, for the register budget
+  router_row<NW, (NW <= 2), false>(x, wr, bias, logits, S, d, E, blockIdx.x, red);
 }
 
 // one wave per token
@@ -22,19 +21,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w, int S, int E,
                                                    int topk, int renorm) {
-  __shared__ float sl[4][8];
-  __shared__ int se[4][8];
+  __shared__ TopkLds L[4];
   const int wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= S) return;
-  topk_token(logits, ids, w, E, topk, renorm, t, sl[wv], se[wv]);
+  topk_token<false>(logits, ids, w, nullptr, E, topk, renorm, t, L[wv]);
 }
 
 template <int NW>
 void launch_router(const moe_dims& m, const uint16_t* x, const float* wr, const float* bias,
                    float* logits, hipStream_t stream) {
-  hipLaunchKernelGGL(router_logits_kernel<NW>, dim3(m.E), dim3(256), 0, stream, x, wr, bias,
-                     logits, m.S, m.d, m.E);
+  hipLaunchKernelGGL(router_logits_kernel<NW>, dim3(m.E), dim3(kRouteThreads), 0, stream, x, wr,
+                     bias, logits, m.S, m.d, m.E);
 }
 
 }  // namespace
@@ -45,9 +43,7 @@ void launch_router_logits(const moe_dims& m, const void* x, const float* wr, con
   switch (router_nw(m.d)) {
     case 1: launch_router<1>(m, xx, wr, bias, logits, stream); break;
     case 2: launch_router<2>(m, xx, wr, bias, logits, stream); break;
-    case 4: launch_router<4>(m, xx, wr, bias, logits, stream); break;
-    case 8: launch_router<8>(m, xx, wr, bias, logits, stream); break;
-    default: launch_router<16>(m, xx, wr, bias, logits, stream); break;
+    default: launch_router<4>(m, xx, wr, bias, logits, stream); break;
   }
 }
 

@@ -12,7 +12,7 @@
 
 namespace moeblk {
 
-constexpr int kTok = 8;  // tokens a wave sums at once
+constexpr int kTok = 8;  // tokens a router wave sums at once
 
 // 8 per-lane partial sums -> wave totals; lane l (l % 8 == 0) holds the total of
 // value index ((l >> 5) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 3) & 1). Each step
@@ -53,22 +53,33 @@ __device__ __forceinline__ float dot4(uint2 xb, f32x4_t w, float a) {
   return a;
 }
 
-// float4s of one wave's K quarter a lane loads: the router kernels are
-// instantiated for NW in {1, 2, 4, 8, 16}
+// A router workgroup: 16 waves, each summing one sixteenth of K.
+constexpr int kRouteWaves = 16;
+constexpr int kRouteThreads = kRouteWaves * kWave;
+
+// float4s of one wave's K slice a lane loads (d <= 16384): NW in {1, 2, 4}
 inline int router_nw(int d) {
-  const int nw = (d / 16 + kWave - 1) / kWave;
-  return nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : 16;
+  const int nf = d / (4 * kRouteWaves);
+  return nf <= kWave ? 1 : nf <= 2 * kWave ? 2 : 4;
 }
 
-// Workgroup-level: logits of expert row e for all S tokens (256 threads). Its
-// 4 waves split K into quarters; lane l takes the float4s l, l + 64, .. (NW of
-// them) of its wave's quarter. The router row is loaded once, all of it in
-// flight at once (non-temporal: it is read once); activations stream in tiles
-// of 8 tokens (with DB, the next tile's loads issue before the current tile is
-// summed). Loads past the quarter are clamped to its last float4 and not
-// summed. Partial sums: a fixed shuffle tree, then the 4 quarters through LDS
-// `red` [4][8] in wave order.
-template <int NW, bool DB>
+// a logit store; kCoh: device-coherent (written through past this XCD's L2,
+// for a reader on another XCD within the same launch)
+template <bool kCoh>
+__device__ __forceinline__ void store_logit(float* p, float v) {
+  if constexpr (kCoh) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
+// Workgroup-level (kRouteThreads): logits of expert row e for all S tokens.
+// Wave w sums K slice w; lane l takes the float4s l, l + 64, .. (NW of them)
+// of the slice. The router row is loaded once, all of it in flight at once
+// (non-temporal: it is read once); activations stream in tiles of 8 tokens
+// (with DB, the next tile's loads issue before the current tile is summed).
+// Loads past the slice are clamped to its last float4 and not summed. Partial
+// sums: a fixed shuffle tree in the wave, then a fixed pairwise tree over the
+// 16 slices through LDS `red`.
+template <int NW, bool DB, bool kCoh>
 __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
                                            const float* __restrict__ wr,
                                            const float* __restrict__ bias,
@@ -76,8 +87,8 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
                                            float (*red)[kTok]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
-  const int kq = d / 4;   // K of one wave
-  const int nf = kq / 4;  // its float4s
+  const int kq = d / kRouteWaves;  // K of one wave
+  const int nf = kq / 4;           // its float4s
   const int k0 = w * kq;
   int f[NW];
   bool live[NW];
@@ -117,8 +128,13 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
     __syncthreads();
     if (threadIdx.x < kTok && t0 + static_cast<int>(threadIdx.x) < S) {
       const int t = threadIdx.x;
-      logits[static_cast<size_t>(t0 + t) * E + e] =
-          ((red[0][t] + red[1][t]) + (red[2][t] + red[3][t])) + b;
+      float q[kRouteWaves / 2];
+#pragma unroll
+      for (int i = 0; i < kRouteWaves / 2; ++i) q[i] = red[2 * i][t] + red[2 * i + 1][t];
+#pragma unroll
+      for (int i = 0; i < kRouteWaves / 4; ++i) q[i] = q[2 * i] + q[2 * i + 1];
+      const float sum = (q[0] + q[1]) + (q[2] + q[3]);
+      store_logit<kCoh>(&logits[static_cast<size_t>(t0 + t) * E + e], sum + b);
     }
   };
   const int n_tiles = (S + kTok - 1) / kTok;
@@ -148,25 +164,42 @@ __device__ __forceinline__ uint32_t order_key(float l) {
 
 __device__ __forceinline__ int popc_ballot(bool p) { return __popcll(__ballot(p)); }
 
+// LDS scratch of one wave's top-k
+struct TopkLds {
+  uint32_t key[8];  // the selected experts, compacted: order keys,
+  int32_t id[8];    // expert ids,
+  float lg[8];      // logits
+  float sl[8];      // the same in slot order
+  int32_t se[8];
+};
+
 // Wave-level: the top-k of token t; lane l holds experts l, l + 64, l + 128,
 // l + 192 (E <= 256).
 // 1. Radix select on the order keys: the k-th largest key T (32 ballot steps).
 // 2. Keys above T are in; keys equal to T are taken lowest id first.
-// 3. A selected expert's slot is the number of selected ones ranking above it
-//    (larger logit, or equal logit and lower id).
+// 3. The k selected are compacted into LDS; lane s < k ranks entry s against
+//    the others (larger logit, or equal logit and lower id, ranks first): its
+//    slot.
 // 4. Sigmoid scores, renormalised by their sum in slot order.
-// sl / se: this wave's 8-entry LDS scratch.
+// kCoh: the logits were written in the same launch by other workgroups (read
+// past this XCD's L2). ids_lds: if not NULL, the ids are also written there
+// ([t * topk + slot]).
+template <bool kCoh>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
-                                           int E, int topk, int renorm, int t, float* sl,
-                                           int* se) {
+                                           int32_t* ids_lds, int E, int topk, int renorm, int t,
+                                           TopkLds& L) {
   const int lane = threadIdx.x & (kWave - 1);
   float lg[4];
   uint32_t key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + kWave * j;
-    lg[j] = e < E ? logits[static_cast<size_t>(t) * E + e] : 0.0f;
+    const float* p = logits + static_cast<size_t>(t) * E + e;
+    if constexpr (kCoh)
+      lg[j] = e < E ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+    else
+      lg[j] = e < E ? *p : 0.0f;
     key[j] = e < E ? order_key(lg[j]) : 0u;
   }
   uint32_t T = 0;
@@ -182,43 +215,41 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
   for (int j = 0; j < 4; ++j) gt += popc_ballot(key[j] > T);
   const int need = topk - gt;  // ties at T still to take
   const uint64_t below = (1ull << lane) - 1ull;
-  bool sel[4];
-  int before = 0;
+  int before = 0, nsel = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint64_t eq = __ballot(key[j] == T);
     const int r = before + __popcll(eq & below);
-    sel[j] = key[j] > T || (key[j] == T && r < need);
+    const bool sel = key[j] > T || (key[j] == T && r < need);
     before += __popcll(eq);
-  }
-  int slot[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint64_t m = __ballot(sel[j]);
-    while (m) {
-      const int src = __builtin_ctzll(m);
-      m &= m - 1ull;
-      const uint32_t ks = __shfl(key[j], src, kWave);
-      const int es = src + kWave * j;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int e = lane + kWave * jj;
-        slot[jj] += (ks > key[jj] || (ks == key[jj] && es < e)) ? 1 : 0;
-      }
+    const uint64_t ms = __ballot(sel);
+    if (sel) {
+      const int pos = nsel + __popcll(ms & below);
+      L.key[pos] = key[j];
+      L.id[pos] = lane + kWave * j;
+      L.lg[pos] = lg[j];
     }
+    nsel += __popcll(ms);
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (sel[j]) {
-      sl[slot[j]] = lg[j];
-      se[slot[j]] = lane + kWave * j;
-    }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+  __builtin_amdgcn_wave_barrier();
+  if (lane < topk) {
+    const uint32_t k = L.key[lane];
+    const int id = L.id[lane];
+    int slot = 0;
+    for (int q = 0; q < topk; ++q) {
+      const uint32_t kq = L.key[q];
+      slot += (kq > k || (kq == k && L.id[q] < id)) ? 1 : 0;
+    }
+    L.sl[slot] = L.lg[lane];
+    L.se[slot] = id;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
   float sc[8], sum = 0.0f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    sc[s] = s < topk ? 1.0f / (1.0f + expf(-sl[s])) : 0.0f;
+    sc[s] = s < topk ? 1.0f / (1.0f + expf(-L.sl[s])) : 0.0f;
     sum += sc[s];
   }
   if (lane < topk) {
@@ -226,7 +257,9 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       if (s == lane) mine = sc[s];
-    ids[static_cast<size_t>(t) * topk + lane] = se[lane];
+    const int id = L.se[lane];
+    ids[static_cast<size_t>(t) * topk + lane] = id;
+    if (ids_lds) ids_lds[t * topk + lane] = id;
     w[static_cast<size_t>(t) * topk + lane] = renorm ? mine / sum : mine;
   }
   __builtin_amdgcn_wave_barrier();

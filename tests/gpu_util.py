@@ -48,6 +48,8 @@ def run_gpu(inp: dict, blk: MoeBlock | None = None, fused: bool = False) -> dict
     else:
         blk.step()
     torch.cuda.synchronize()
+    err = blk.forward_error() if fused else blk.ffn_error()
+    assert err == 0, "a wait in the expert-FFN launch hit its bound"
     return dict(
         blk=blk, fused=fused, logits=to_np(blk.logits), ids=to_np(blk.ids), w=to_np(blk.w), counts=to_np(blk.counts),
         offsets=to_np(blk.offsets), rows=to_np(blk.rows), pick_pos=to_np(blk.pick_pos),
