@@ -32,12 +32,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ rows,
     int32_t* __restrict__ pick_pos, int32_t* __restrict__ active, int S, int E, int topk,
     int renorm, int n_loc, int local_base, int R_max) {
-  __shared__ TopkLds tl[kTopkThreads / kWave];
   __shared__ BucketLds L;
   __shared__ int32_t ids_l[kMaxTokens * 8];
   const int wv = threadIdx.x >> 6;
   for (int t = wv; t < S; t += kTopkThreads / kWave)
-    topk_token<false>(logits, ids, w, ids_l, E, topk, renorm, t, tl[wv]);
+    topk_token<false>(logits, ids, w, ids_l, E, topk, renorm, t);
   __syncthreads();
   bucket_block(ids_l, S, topk, n_loc, local_base, R_max, L, nullptr, true, counts, offsets, rows,
                pick_pos, active);

@@ -21,11 +21,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w, int S, int E,
                                                    int topk, int renorm) {
-  __shared__ TopkLds L[4];
-  const int wv = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wv;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= S) return;
-  topk_token<false>(logits, ids, w, nullptr, E, topk, renorm, t, L[wv]);
+  topk_token<false>(logits, ids, w, nullptr, E, topk, renorm, t);
 }
 
 template <int NW>

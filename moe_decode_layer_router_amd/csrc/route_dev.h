@@ -162,107 +162,120 @@ __device__ __forceinline__ uint32_t order_key(float l) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int popc_ballot(bool p) { return __popcll(__ballot(p)); }
+// the logit of an order key (-0 comes back as +0)
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 
-// LDS scratch of one wave's top-k
-struct TopkLds {
-  uint32_t key[8];  // the selected experts, compacted: order keys,
-  int32_t id[8];    // expert ids,
-  float lg[8];      // logits
-  float sl[8];      // the same in slot order
-  int32_t se[8];
-};
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// maximum over the wave, in every lane: within each row of 16 lanes by DPP
+// (pair swap, quad swap, half-row mirror, row mirror), then over the 4 rows
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax32(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = umax32(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = umax32(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  v = umax32(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+  return umax32(umax32(r0, r1), umax32(r2, r3));
+}
+
+// (ka, ia) ranks before (kb, ib): larger key, or equal key and lower id
+__device__ __forceinline__ bool ranks_before(uint32_t ka, int ia, uint32_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+__device__ __forceinline__ void order2(uint32_t& ka, int& ia, uint32_t& kb, int& ib) {
+  if (ranks_before(kb, ib, ka, ia)) {
+    const uint32_t k = ka;
+    const int i = ia;
+    ka = kb;
+    ia = ib;
+    kb = k;
+    ib = i;
+  }
+}
 
 // Wave-level: the top-k of token t; lane l holds experts l, l + 64, l + 128,
 // l + 192 (E <= 256).
-// 1. Radix select on the order keys: the k-th largest key T (32 ballot steps).
-// 2. Keys above T are in; keys equal to T are taken lowest id first.
-// 3. The k selected are compacted into LDS; lane s < k ranks entry s against
-//    the others (larger logit, or equal logit and lower id, ranks first): its
-//    slot.
-// 4. Sigmoid scores, renormalised by their sum in slot order.
+// 1. Each lane orders its 4 experts (larger logit first, equal logits lower id
+//    first): a 5-comparator network.
+// 2. k rounds: the wave maximum of the lanes' first keys is the next slot;
+//    among lanes tied at that key the lowest expert id wins; the winning lane
+//    drops its first entry.
+// 3. Lane s < k holds slot s: sigmoid score, renormalised by the sum of the k
+//    scores in slot order.
 // kCoh: the logits were written in the same launch by other workgroups (read
 // past this XCD's L2). ids_lds: if not NULL, the ids are also written there
 // ([t * topk + slot]).
 template <bool kCoh>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
-                                           int32_t* ids_lds, int E, int topk, int renorm, int t,
-                                           TopkLds& L) {
+                                           int32_t* ids_lds, int E, int topk, int renorm, int t) {
   const int lane = threadIdx.x & (kWave - 1);
-  float lg[4];
-  uint32_t key[4];
+  uint32_t k[4];
+  int id[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + kWave * j;
     const float* p = logits + static_cast<size_t>(t) * E + e;
-    if constexpr (kCoh)
-      lg[j] = e < E ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
-    else
-      lg[j] = e < E ? *p : 0.0f;
-    key[j] = e < E ? order_key(lg[j]) : 0u;
-  }
-  uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = T | (1u << b);
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) n += popc_ballot(key[j] >= c);
-    if (n >= topk) T = c;
-  }
-  int gt = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) gt += popc_ballot(key[j] > T);
-  const int need = topk - gt;  // ties at T still to take
-  const uint64_t below = (1ull << lane) - 1ull;
-  int before = 0, nsel = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint64_t eq = __ballot(key[j] == T);
-    const int r = before + __popcll(eq & below);
-    const bool sel = key[j] > T || (key[j] == T && r < need);
-    before += __popcll(eq);
-    const uint64_t ms = __ballot(sel);
-    if (sel) {
-      const int pos = nsel + __popcll(ms & below);
-      L.key[pos] = key[j];
-      L.id[pos] = lane + kWave * j;
-      L.lg[pos] = lg[j];
+    float lg = 0.0f;
+    if (e < E) {
+      if constexpr (kCoh) lg = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else lg = *p;
     }
-    nsel += __popcll(ms);
+    k[j] = e < E ? order_key(lg) : 0u;  // 0: below every expert
+    id[j] = e;
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-  __builtin_amdgcn_wave_barrier();
-  if (lane < topk) {
-    const uint32_t k = L.key[lane];
-    const int id = L.id[lane];
-    int slot = 0;
-    for (int q = 0; q < topk; ++q) {
-      const uint32_t kq = L.key[q];
-      slot += (kq > k || (kq == k && L.id[q] < id)) ? 1 : 0;
+  order2(k[0], id[0], k[1], id[1]);
+  order2(k[2], id[2], k[3], id[3]);
+  order2(k[0], id[0], k[2], id[2]);
+  order2(k[1], id[1], k[3], id[3]);
+  order2(k[1], id[1], k[2], id[2]);
+
+  uint32_t my_key = 0;
+  int my_id = 0;
+  for (int r = 0; r < topk; ++r) {
+    const uint32_t m = wave_max_u32(k[0]);
+    const uint64_t tie = __ballot(k[0] == m);
+    int wl = __builtin_ctzll(tie);
+    int wid = __builtin_amdgcn_readlane(id[0], wl);
+    if (__popcll(tie) > 1) {  // equal logits: the lowest expert id
+      uint64_t rest = tie & (tie - 1ull);
+      while (rest) {
+        const int l = __builtin_ctzll(rest);
+        rest &= rest - 1ull;
+        const int il = __builtin_amdgcn_readlane(id[0], l);
+        if (il < wid) {
+          wid = il;
+          wl = l;
+        }
+      }
     }
-    L.sl[slot] = L.lg[lane];
-    L.se[slot] = id;
+    if (lane == r) {
+      my_key = m;
+      my_id = wid;
+    }
+    if (lane == wl) {
+      k[0] = k[1];
+      id[0] = id[1];
+      k[1] = k[2];
+      id[1] = id[2];
+      k[2] = k[3];
+      id[2] = id[3];
+      k[3] = 0u;
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_wave_barrier();
-  float sc[8], sum = 0.0f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    sc[s] = s < topk ? 1.0f / (1.0f + expf(-L.sl[s])) : 0.0f;
-    sum += sc[s];
-  }
+  const float sc = 1.0f / (1.0f + expf(-key_logit(my_key)));
+  float sum = 0.0f;
+  for (int q = 0; q < topk; ++q)
+    sum += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sc), q));
   if (lane < topk) {
-    float mine = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (s == lane) mine = sc[s];
-    const int id = L.se[lane];
-    ids[static_cast<size_t>(t) * topk + lane] = id;
-    if (ids_lds) ids_lds[t * topk + lane] = id;
-    w[static_cast<size_t>(t) * topk + lane] = renorm ? mine / sum : mine;
+    ids[static_cast<size_t>(t) * topk + lane] = my_id;
+    if (ids_lds) ids_lds[t * topk + lane] = my_id;
+    w[static_cast<size_t>(t) * topk + lane] = renorm ? sc / sum : sc;
   }
-  __builtin_amdgcn_wave_barrier();
 }
 
 }  // namespace moeblk
