@@ -74,7 +74,13 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
 // the single launch (S <= 16: one group of 16 rows an item, no shared expert);
 // PG / PD: chunks in flight a wave in gate_up / down tasks
 template <int PG, int PD>
-__global__ __launch_bounds__(kSplit * kWave, 4) void ffn_single_kernel(FfnArgs a) {
+#ifndef MOE_SINGLE_PD
+#define MOE_SINGLE_PD 2  // down chunks in flight a wave (issued before the wait)
+#endif
+#ifndef MOE_SINGLE_OCC
+#define MOE_SINGLE_OCC 4  // workgroups a CU
+#endif
+__global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_kernel(FfnArgs a) {
   __shared__ f32x4_t red[kSplit][1][4][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
@@ -226,7 +232,7 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   const bool big = ffn_group(m) > 16;
   if (single_launch(m)) {
     const int grid = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
-    hipLaunchKernelGGL((ffn_single_kernel<2, 2>), dim3(grid), dim3(kSplit * kWave), 0, stream, a);
+    hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD>), dim3(grid), dim3(kSplit * kWave), 0, stream, a);
   } else if (m.shared_I) big ? launch_pair<2, 2, 2, true>(a, stream) : launch_pair<1, 2, 4, true>(a, stream);
   else big ? launch_pair<2, 2, 2, false>(a, stream) : launch_pair<1, 2, 4, false>(a, stream);
   return launch_status();

@@ -155,6 +155,9 @@ FUSED = {
     "d640_I256": _tiny(S=6, d=640, I=256, E=16, n_local=4, local_base=4, topk=3),
     "d7168_S33": _tiny(S=33, d=7168, I=128, E=32, n_local=8, topk=8),
     "no_local": _tiny(S=12, E=16, n_local=4, local_base=8, topk=2, bias_kind="local", beta=-50.0),
+    "S1": _tiny(S=1),
+    "some_local": _tiny(S=16, E=32, n_local=4, local_base=8, topk=2),
+    "d4096_S16": _tiny(S=16, d=4096, I=256, E=16, n_local=8, topk=4),
 }
 
 KEYS = ("logits", "ids", "w", "counts", "offsets", "rows", "pick_pos", "active", "out")
@@ -162,10 +165,13 @@ KEYS = ("logits", "ids", "w", "counts", "offsets", "rows", "pick_pos", "active",
 
 @pytest.mark.parametrize("name", list(FUSED))
 def test_fused_equals_four_calls(name):
-    """moe_forward runs the same device code in the same order as the four
-    calls: every output is bit-identical, and both match the oracle."""
+    """moe_forward computes every value with the same device code as the four
+    calls: every output is bit-identical, and both match the oracle. The out
+    rows are poisoned in between, so every row must be written again (also
+    the zero rows of tokens without a local pick)."""
     inp = make_inputs(FUSED[name], 11, gamma="random")
     g4 = run_gpu(inp)
+    g4["blk"].out.fill_(float("nan"))
     g1 = run_gpu(inp, g4["blk"], fused=True)
     for k in KEYS:
         assert np.array_equal(g1[k], g4[k]), k
@@ -177,7 +183,9 @@ def test_fused_equals_four_calls(name):
     check_block(inp, g1, strict=(name in ("tiny", "no_local")))
 
 
-@pytest.mark.parametrize("name,n_tok", [("s8_uniform", 8), ("s64_zipf", 3), ("s128_shared", 2)])
+@pytest.mark.parametrize(
+    "name,n_tok", [("s8_uniform", 8), ("s16_local25", 4), ("s64_zipf", 3), ("s128_shared", 2)]
+)
 def test_fused_full_workload(name, n_tok):
     cfg = get_config(name)
     inp = make_inputs(cfg, 0, gamma="random")
