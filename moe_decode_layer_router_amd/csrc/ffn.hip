@@ -73,13 +73,13 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
 
 // the single launch (S <= 16: one group of 16 rows an item, no shared expert);
 // PG / PD: chunks in flight a wave in gate_up / down tasks
-template <int PG, int PD>
 #ifndef MOE_SINGLE_PD
 #define MOE_SINGLE_PD 2  // down chunks in flight a wave (issued before the wait)
 #endif
 #ifndef MOE_SINGLE_OCC
 #define MOE_SINGLE_OCC 4  // workgroups a CU
 #endif
+template <int PG, int PD>
 __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_kernel(FfnArgs a) {
   __shared__ f32x4_t red[kSplit][1][4][kWave];
   const int lane = threadIdx.x & (kWave - 1);
