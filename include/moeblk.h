@@ -212,9 +212,10 @@ int moe_combine(const moe_dims* dims, const void* y, const float* topk_w, const 
 size_t moe_forward_workspace_bytes(const moe_dims* dims);
 
 /* The whole block -- the work of moe_route, moe_bucket, moe_expert_ffn and
- * moe_combine -- with one launch fewer than the four calls: top-k and
- * bucketing share one workgroup. Arguments and outputs are those of the four calls, with
- * identical values (the same device code runs in the same order). `workspace`
+ * moe_combine -- on one stream. For S <= 16 top-k and bucketing share one
+ * workgroup (one launch fewer than the four calls); beyond, the launches are
+ * those of the four calls. Arguments and outputs are those of the four calls,
+ * with identical values (the same device code computes every value). `workspace`
  * follows the moe_expert_ffn rules (zero-filled once before first use, error
  * word at byte moe_forward_workspace_bytes - 256, calls sharing it must not
  * overlap). */

@@ -1,7 +1,8 @@
 // forward.hip -- moe_forward: the whole block as five launches on one stream.
 //
 //   1  router logits (one workgroup an expert row)
-//   2  top-k of every token and the bucketing, in one workgroup
+//   2  top-k of every token and the bucketing, in one workgroup (S <= 16;
+//      beyond, one wave a token in its own launch, then the bucketing)
 //   3  the expert FFNs: gate_up + SwiGLU, then down (shared expert included)
 //   4  per-pick RMSNorm and the weighted sum (one workgroup a token)
 //
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
   __shared__ int32_t ids_l[kMaxTokens * 8];
   const int wv = threadIdx.x >> 6;
   for (int t = wv; t < S; t += kTopkThreads / kWave)
-    topk_token<false>(logits, ids, w, ids_l, E, topk, renorm, t);
+    topk_token(logits, ids, w, ids_l, E, topk, renorm, t);
   __syncthreads();
   bucket_block(ids_l, S, topk, n_loc, local_base, R_max, L, nullptr, true, counts, offsets, rows,
                pick_pos, active);
@@ -77,9 +78,14 @@ extern "C" int moe_forward(const moe_dims* dims, const void* x, const float* w_r
   MOE_REQUIRE(workspace_bytes >= moe_forward_workspace_bytes(dims), MOE_ERR_WORKSPACE);
 
   launch_router_logits(m, x, w_router, bias, logits, stream);
-  hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits, topk_ids,
-                     topk_w, counts, offsets, rows, pick_pos, active, m.S, m.E, m.topk, m.renorm,
-                     m.n_local, m.local_base, r_max(m));
+  if (m.S <= kTopkThreads / kWave) {
+    hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits, topk_ids,
+                       topk_w, counts, offsets, rows, pick_pos, active, m.S, m.E, m.topk, m.renorm,
+                       m.n_local, m.local_base, r_max(m));
+  } else {  // a wave a token needs more waves than one workgroup holds
+    launch_topk(m, logits, topk_ids, topk_w, stream);
+    launch_bucket(m, topk_ids, counts, offsets, rows, pick_pos, active, stream);
+  }
   const int frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y,
                              workspace, stream);
   if (frc) return frc;

@@ -6,14 +6,15 @@
 namespace moeblk {
 namespace {
 
-// one workgroup an expert row
+// one workgroup an expert row: the row streams from HBM once, all of it in
+// flight at once; every workgroup reads all of x (through L2)
 template <int NW>
 __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     float* __restrict__ logits, int S, int d, int E) {
-  __shared__ float red[kRouteWaves][kTok];
+  __shared__ float red[kMaxRouteTiles][kRouteWaves][kTok];
   // NW = 4 (d > 8192): one tile buffer, for the register budget
-  router_row<NW, (NW <= 2), false>(x, wr, bias, logits, S, d, E, blockIdx.x, red);
+  router_row<NW, (NW <= 2)>(x, wr, bias, logits, S, d, E, blockIdx.x, red);
 }
 
 // one wave per token
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int topk, int renorm) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= S) return;
-  topk_token<false>(logits, ids, w, nullptr, E, topk, renorm, t);
+  topk_token(logits, ids, w, nullptr, E, topk, renorm, t);
 }
 
 template <int NW>

@@ -13,6 +13,7 @@
 namespace moeblk {
 
 constexpr int kTok = 8;  // tokens a router wave sums at once
+constexpr int kMaxRouteTiles = 128 / kTok;  // S <= 128
 
 // 8 per-lane partial sums -> wave totals; lane l (l % 8 == 0) holds the total of
 // value index ((l >> 5) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 3) & 1). Each step
@@ -63,28 +64,21 @@ inline int router_nw(int d) {
   return nf <= kWave ? 1 : nf <= 2 * kWave ? 2 : 4;
 }
 
-// a logit store; kCoh: device-coherent (written through past this XCD's L2,
-// for a reader on another XCD within the same launch)
-template <bool kCoh>
-__device__ __forceinline__ void store_logit(float* p, float v) {
-  if constexpr (kCoh) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
-
 // Workgroup-level (kRouteThreads): logits of expert row e for all S tokens.
 // Wave w sums K slice w; lane l takes the float4s l, l + 64, .. (NW of them)
 // of the slice. The router row is loaded once, all of it in flight at once
 // (non-temporal: it is read once); activations stream in tiles of 8 tokens
 // (with DB, the next tile's loads issue before the current tile is summed).
 // Loads past the slice are clamped to its last float4 and not summed. Partial
-// sums: a fixed shuffle tree in the wave, then a fixed pairwise tree over the
-// 16 slices through LDS `red`.
-template <int NW, bool DB, bool kCoh>
+// sums: a fixed shuffle tree in the wave into LDS `red` [tile][wave][token]
+// (no barrier between tiles, so the waves stream their tiles independently),
+// then, after one barrier, a fixed pairwise tree over the 16 slices.
+template <int NW, bool DB>
 __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
                                            const float* __restrict__ wr,
                                            const float* __restrict__ bias,
                                            float* __restrict__ logits, int S, int d, int E, int e,
-                                           float (*red)[kTok]) {
+                                           float (*red)[kRouteWaves][kTok]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
   const int kq = d / kRouteWaves;  // K of one wave
@@ -123,19 +117,7 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
     }
     const float v = reduce8(acc, lane);
     const int tok = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
-    __syncthreads();  // red of the previous tile consumed
-    if ((lane & 7) == 0) red[w][tok] = v;
-    __syncthreads();
-    if (threadIdx.x < kTok && t0 + static_cast<int>(threadIdx.x) < S) {
-      const int t = threadIdx.x;
-      float q[kRouteWaves / 2];
-#pragma unroll
-      for (int i = 0; i < kRouteWaves / 2; ++i) q[i] = red[2 * i][t] + red[2 * i + 1][t];
-#pragma unroll
-      for (int i = 0; i < kRouteWaves / 4; ++i) q[i] = q[2 * i] + q[2 * i + 1];
-      const float sum = (q[0] + q[1]) + (q[2] + q[3]);
-      store_logit<kCoh>(&logits[static_cast<size_t>(t0 + t) * E + e], sum + b);
-    }
+    if ((lane & 7) == 0) red[t0 / kTok][w][tok] = v;
   };
   const int n_tiles = (S + kTok - 1) / kTok;
   if constexpr (!DB) {
@@ -152,6 +134,18 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
       if (tile + 2 < n_tiles) load_tile(xa, (tile + 2) * kTok);
       sum_tile(xb, (tile + 1) * kTok);
     }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < S; t += blockDim.x) {
+    const float(*rt)[kTok] = red[t / kTok];
+    const int j = t % kTok;
+    float q[kRouteWaves / 2];
+#pragma unroll
+    for (int i = 0; i < kRouteWaves / 2; ++i) q[i] = rt[2 * i][j] + rt[2 * i + 1][j];
+#pragma unroll
+    for (int i = 0; i < kRouteWaves / 4; ++i) q[i] = q[2 * i] + q[2 * i + 1];
+    const float sum = (q[0] + q[1]) + (q[2] + q[3]);
+    logits[static_cast<size_t>(t) * E + e] = sum + b;
   }
 }
 
@@ -206,10 +200,7 @@ __device__ __forceinline__ void order2(uint32_t& ka, int& ia, uint32_t& kb, int&
 //    drops its first entry.
 // 3. Lane s < k holds slot s: sigmoid score, renormalised by the sum of the k
 //    scores in slot order.
-// kCoh: the logits were written in the same launch by other workgroups (read
-// past this XCD's L2). ids_lds: if not NULL, the ids are also written there
-// ([t * topk + slot]).
-template <bool kCoh>
+// ids_lds: if not NULL, the ids are also written there ([t * topk + slot]).
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
                                            int32_t* ids_lds, int E, int topk, int renorm, int t) {
@@ -220,12 +211,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
   for (int j = 0; j < 4; ++j) {
     const int e = lane + kWave * j;
     const float* p = logits + static_cast<size_t>(t) * E + e;
-    float lg = 0.0f;
-    if (e < E) {
-      if constexpr (kCoh) lg = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else lg = *p;
-    }
-    k[j] = e < E ? order_key(lg) : 0u;  // 0: below every expert
+    k[j] = e < E ? order_key(*p) : 0u;  // 0: below every expert
     id[j] = e;
   }
   order2(k[0], id[0], k[1], id[1]);
