@@ -117,4 +117,9 @@ def dense_block(inp: dict, ids: np.ndarray | None = None) -> dict:
             for slot in range(k):
                 if ids[t, slot] == cfg.local_base + el:
                     out[t] += float(w[t, slot]) * z[t]
+    if cfg.shared_I:  # always-on dense expert, weight 1, no norm
+        Is = cfg.shared_I
+        gus = bf16_val(nearest_bf16_bits(x @ bf16_val(inp["ws13"]).T))  # [S, 2 Is]
+        hs = bf16_val(nearest_bf16_bits(silu_hp(gus[:, :Is]) * gus[:, Is:]))
+        out += bf16_val(nearest_bf16_bits(hs @ bf16_val(inp["ws2"]).T))
     return dict(logits=logits, ids=ids, w=w, y_all=y_all, out=out)

@@ -145,6 +145,19 @@ def test_full_workload(name, n_tok):
     check_block(inp, g, tokens=_sample_tokens(g, cfg, n_tok), strict=True)
 
 
+@pytest.mark.parametrize("S", [32, 96])
+def test_more_row_counts(S):
+    """The K5 page's other row counts (S = 32, 96) on the S = 8 workload's
+    shapes and routing, through both entry points."""
+    cfg = get_config("s8_uniform").with_(name=f"s{S}_uniform", S=S)
+    inp = make_inputs(cfg, 1, gamma="random")
+    g = run_gpu(inp)
+    check_block(inp, g, tokens=_sample_tokens(g, cfg, 3), strict=True)
+    g1 = run_gpu(inp, g["blk"], fused=True)
+    for k in ("ids", "w", "counts", "rows", "pick_pos", "out"):
+        assert np.array_equal(g1[k], g[k]), k
+
+
 # ------------------------------------------------------------ moe_forward
 
 FUSED = {

@@ -38,6 +38,27 @@ def test_tiny_block_equals_dense_brute_force(seed, gamma):
     np.testing.assert_allclose(got["out"], ref["out"], rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize(
+    "kw",
+    [
+        dict(S=6, E=16, n_local=4, local_base=8, topk=3, renorm=0),
+        dict(S=5, E=12, n_local=3, local_base=3, topk=4, bias_kind="local", beta=0.3),
+        dict(S=4, E=8, n_local=8, topk=2, shared_I=128),
+        dict(S=7, E=16, n_local=4, local_base=12, topk=2, shared_I=256),
+    ],
+)
+def test_block_equals_dense_brute_force_general(kw):
+    """Non-local picks, a local range not at 0, renorm off, a routing bias and
+    the shared expert, against the independent dense evaluation."""
+    cfg = get_config("tiny").with_(**kw)
+    inp = make_inputs(cfg, 4, gamma="random")
+    got = oracle.forward(inp)
+    ref = dense_block(inp)
+    assert np.array_equal(got["ids"], ref["ids"])
+    assert np.array_equal(got["w"], ref["w"])
+    np.testing.assert_allclose(got["out"], ref["out"], rtol=1e-6, atol=1e-6)
+
+
 def _one_expert(d=256, I=128, seed=0):  # noqa: E741
     rng = np.random.default_rng(seed)
     x = f32_to_bf16_bits(rng.standard_normal(d, dtype=np.float32))
