@@ -16,8 +16,8 @@ does between the other layers' weights.
 
 Output: one JSON line (see the fields below). ``roofline`` covers the dominant
 work, the expert FFN (one moe_expert_ffn call, about 95% of a step's bytes: one
-kernel for S <= 16 without a shared expert, else a gate_up + SwiGLU kernel and
-a down kernel), timed with HIP events around each call on the stream its
+kernel without a shared expert, else a gate_up + SwiGLU kernel and a down
+kernel), timed with HIP events around each call on the stream its
 kernels run on, in a separate timed pass; its
 ``traffic`` comes from the committed rocprofv3 counter summary when that
 summary was taken on the current kernel sources, else null.
@@ -197,8 +197,8 @@ def main() -> int:
     if cfg.shared_I:
         b_ffn += cfg.S * cfg.shared_I * 2 * 2 + cfg.S * cfg.d * 2
     achieved = b_ffn / (ffn_ms * 1e-3) / 1e9
-    # S <= 16 without a shared expert: one launch; else gate_up, then down
-    single = cfg.S <= 16 and not cfg.shared_I
+    # without a shared expert: one launch; else gate_up, then down
+    single = not cfg.shared_I
     ffn_kernels = "moe_expert_ffn: " + ("ffn_single_kernel" if single else "gate_up_kernel + down_kernel")
     traffic = committed_traffic(cfg.name)
 

@@ -182,10 +182,10 @@ size_t moe_ffn_workspace_bytes(const moe_dims* dims);
  *              does; that call's outputs are undefined and the workspace must
  *              be zero-filled again).
  * The down GEMM of an expert needs all of its SwiGLU rows (K3 page, stages
- * "C, D"). For S <= 16 without a shared expert the FFNs are one launch: a down
- * task issues its first weight loads, then waits on a counter of its expert's
- * finished gate_up tasks. Otherwise they are two launches, gate_up + SwiGLU
- * then down. */
+ * "C, D"). Without a shared expert the FFNs are one launch: a down task
+ * issues its first weight loads, then waits on a ready flag set once all of
+ * its expert's gate_up tasks are done. With a shared expert they are two
+ * launches, gate_up + SwiGLU then down. */
 int moe_expert_ffn(const moe_dims* dims, const void* x, const void* w13_packed,
                    const void* w2_packed, const int32_t* counts, const int32_t* offsets,
                    const int32_t* rows, const int32_t* active, const void* ws13_packed,

@@ -3,19 +3,20 @@
 // Muse Spark K3 page, stages "C, D": down needs every SwiGLU row of its expert,
 // a dependency across all workgroups of the gate_up stage. Two shapes:
 //
-// * S <= 16 without a shared expert: ONE launch. Workgroup ids run over the
-//   gate_up tasks, then the down tasks (item-major, row block minor), then
-//   workgroups past the last item, which leave at once. Every workgroup reads
-//   the 32 bucket counts first, so the ids of real tasks are dense. A gate_up
-//   task writes its SwiGLU rows through to the coherence point (sc1) and counts
+// * Without a shared expert: ONE launch. Workgroup ids run over the gate_up
+//   tasks, then the down tasks (item-major, row block minor), then workgroups
+//   past the last item, which leave at once. Every workgroup reads the 32
+//   bucket counts first, so the ids of real tasks are dense. A gate_up task
+//   writes its SwiGLU rows through to the coherence point (sc1) and counts
 //   itself in prod[item] once its stores are done; the last one of the item
 //   sets a ready flag for each of the item's down tasks. A down task issues
-//   its first weight loads, then waits for its flag, then reads the SwiGLU rows
-//   with coherent loads: its weights stream while gate_up finishes. At these
-//   sizes every task of the launch fits on the device at once.
-// * otherwise: two launches, gate_up + SwiGLU then down; the kernel boundary
-//   carries the dependency. Grid of each: the shared expert's tasks first,
-//   then the routed items, then workgroups past the last item.
+//   its first weight loads, then waits for its flag, then reads the SwiGLU
+//   rows with coherent loads: its weights stream while gate_up finishes.
+// * With a shared expert: two launches, gate_up + SwiGLU then down; the kernel
+//   boundary carries the dependency. Grid of each: the shared expert's tasks
+//   first, then the routed items, then workgroups past the last item.
+//
+// Work items hold 16 bucket rows for S <= 16, else 32.
 //
 // The host does not know the bucket sizes, so a grid covers the largest
 // possible number of items.
@@ -71,42 +72,51 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
     __hip_atomic_store(&flags[i * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// the single launch (S <= 16: one group of 16 rows an item, no shared expert);
-// PG / PD: chunks in flight a wave in gate_up / down tasks
+// The single launch (no shared expert); TTG token tiles an item, PG / PD:
+// chunks in flight a wave in gate_up / down tasks. Forward progress: every
+// gate_up workgroup id is below every down workgroup id, and workgroups are
+// dispatched in id order, so when a down task waits, every gate_up task has
+// been dispatched; gate_up tasks wait for nothing. A wait is bounded (about a
+// second) and sets the error word if it ever hits the bound.
 #ifndef MOE_SINGLE_PD
 #define MOE_SINGLE_PD 2  // down chunks in flight a wave (issued before the wait)
 #endif
 #ifndef MOE_SINGLE_OCC
 #define MOE_SINGLE_OCC 4  // workgroups a CU
 #endif
-template <int PG, int PD>
-__global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_kernel(FfnArgs a) {
-  __shared__ f32x4_t red[kSplit][1][4][kWave];
+// workgroups a CU for the 32-row groups (more registers a wave)
+#ifndef MOE_SINGLE_OCC2
+#define MOE_SINGLE_OCC2 3
+#endif
+template <int TTG, int PG, int PD>
+__global__ __launch_bounds__(kSplit * kWave, TTG == 1 ? MOE_SINGLE_OCC : MOE_SINGLE_OCC2) void
+ffn_single_kernel(FfnArgs a) {
+  __shared__ f32x4_t red[kSplit][TTG][4][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
-  const int n_work = count_work<1>(cnt);
+  const int n_work = count_work<TTG>(cnt);
   const int RB13 = 2 * a.I / kRowsPerBlock, NC13 = a.d / kChunkK;
   const int RB2 = a.d / kRowsPerBlock, NC2 = a.I / kChunkK;
   int t = blockIdx.x;
   int el, row0, ntok;
   if (t < n_work * RB13) {
     const int wi = t / RB13, rb = t - wi * RB13;
-    find_task<1>(cnt, wi, el, row0, ntok);
+    find_task<TTG>(cnt, wi, el, row0, ntok);
     const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB13 + rb) * NC13 * kMxTileBytes;
     const int32_t* rows = a.rows;
-    ffn_task<true, 1, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
-                                      [rows](int r) { return rows[r]; }, NoWait{}, red);
+    ffn_task<true, TTG, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
+                                        [rows](int r) { return rows[r]; }, NoWait{}, red);
     publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
     return;
   }
   t -= n_work * RB13;
   if (t >= n_work * RB2) return;
   const int wi = t / RB2, rb = t - wi * RB2;
-  find_task<1>(cnt, wi, el, row0, ntok);
+  find_task<TTG>(cnt, wi, el, row0, ntok);
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB2 + rb) * NC2 * kMxTileBytes;
-  ffn_task<true, 1, PD, false, true>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d,
-                                     [](int r) { return r; }, WaitFlag{&a.ready[t * kCtlStride], a.error},
-                                     red);
+  ffn_task<true, TTG, PD, false, true>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d,
+                                       [](int r) { return r; },
+                                       WaitFlag{&a.ready[t * kCtlStride], a.error}, red);
 }
 
 template <int TTG, int P, bool kShared>
@@ -186,7 +196,7 @@ void launch_pair(const FfnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((down_kernel<TTG, PD, kShared>), dim3(g2), dim3(kSplit * kWave), 0, stream, a);
 }
 
-bool single_launch(const moe_dims& m) { return ffn_group(m) == 16 && m.shared_I == 0; }
+bool single_launch(const moe_dims& m) { return m.shared_I == 0; }
 
 }  // namespace
 
@@ -232,9 +242,14 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   const bool big = ffn_group(m) > 16;
   if (single_launch(m)) {
     const int grid = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
-    hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD>), dim3(grid), dim3(kSplit * kWave), 0, stream, a);
-  } else if (m.shared_I) big ? launch_pair<2, 2, 2, true>(a, stream) : launch_pair<1, 2, 4, true>(a, stream);
-  else big ? launch_pair<2, 2, 2, false>(a, stream) : launch_pair<1, 2, 4, false>(a, stream);
+    if (big)
+      hipLaunchKernelGGL((ffn_single_kernel<2, 2, 2>), dim3(grid), dim3(kSplit * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((ffn_single_kernel<1, 2, MOE_SINGLE_PD>), dim3(grid), dim3(kSplit * kWave), 0,
+                         stream, a);
+  } else {  // a shared expert
+    big ? launch_pair<2, 2, 2, true>(a, stream) : launch_pair<1, 2, 4, true>(a, stream);
+  }
   return launch_status();
 }
 
