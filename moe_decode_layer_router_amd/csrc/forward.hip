@@ -1,14 +1,15 @@
-// forward.hip -- moe_forward: the whole block as five launches on one stream.
+// forward.hip -- moe_forward: the whole block as a chain of launches on one
+// stream.
 //
 //   1  router logits (one workgroup an expert row)
 //   2  top-k of every token and the bucketing, in one workgroup (S <= 16;
 //      beyond, one wave a token in its own launch, then the bucketing)
-//   3  the expert FFNs: gate_up + SwiGLU, then down (shared expert included)
+//   3  the expert FFNs (ffn.hip: one launch, or two with a shared expert)
 //   4  per-pick RMSNorm and the weighted sum (one workgroup a token)
 //
 // The outputs are those of moe_route, moe_bucket, moe_expert_ffn and
-// moe_combine, bit for bit: the same device code runs in the same order.
-// Step 2 replaces two launches of the four-call path. (Measured on MI355X: a
+// moe_combine, bit for bit: the same device code computes every value. For
+// S <= 16, step 2 replaces two launches of the four-call path. (Measured on MI355X: a
 // dependent launch costs about 2.5 us, while a grid-wide barrier inside one
 // launch costs tens of microseconds, so a chain of short launches is faster
 // than one persistent kernel. Handing the logits from the router workgroups to
