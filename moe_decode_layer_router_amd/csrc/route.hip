@@ -17,6 +17,38 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
   router_row<NW, (NW <= 2)>(x, wr, bias, logits, S, d, E, blockIdx.x, red);
 }
 
+// S > 16: kRouteBlockTok tokens x NE router rows a workgroup
+template <int NW, int NE>
+__global__ __launch_bounds__(kRouteThreads) void router_block_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    float* __restrict__ logits, int S, int d, int E) {
+  __shared__ float red[(kRouteBlockTok / kTok) * NE][kRouteWaves][kTok];
+  router_block<NW, NE>(x, wr, bias, logits, S, d, E, NE * blockIdx.x, kRouteBlockTok * blockIdx.y,
+                       red);
+}
+
+template <int NW, int NE>
+void launch_block(const moe_dims& m, const uint16_t* x, const float* wr, const float* bias,
+                  float* logits, hipStream_t stream) {
+  hipLaunchKernelGGL((router_block_kernel<NW, NE>), dim3((m.E + NE - 1) / NE,
+                     (m.S + kRouteBlockTok - 1) / kRouteBlockTok), dim3(kRouteThreads), 0, stream,
+                     x, wr, bias, logits, m.S, m.d, m.E);
+}
+
+// NE: router rows a workgroup, so that about E * S / 16 / NE ~ E workgroups
+// (at most 2 rows for d > 8192, for the register budget)
+template <int NW>
+void launch_blocks(const moe_dims& m, const uint16_t* x, const float* wr, const float* bias,
+                   float* logits, hipStream_t stream) {
+  if constexpr (NW >= 4) {
+    launch_block<NW, 2>(m, x, wr, bias, logits, stream);
+  } else {
+    if (m.S <= 32) launch_block<NW, 2>(m, x, wr, bias, logits, stream);
+    else if (m.S <= 64) launch_block<NW, 4>(m, x, wr, bias, logits, stream);
+    else launch_block<NW, 8>(m, x, wr, bias, logits, stream);
+  }
+}
+
 // one wave per token
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    int32_t* __restrict__ ids,
@@ -39,6 +71,14 @@ void launch_router(const moe_dims& m, const uint16_t* x, const float* wr, const 
 void launch_router_logits(const moe_dims& m, const void* x, const float* wr, const float* bias,
                           float* logits, hipStream_t stream) {
   const uint16_t* xx = static_cast<const uint16_t*>(x);
+  if (m.S > kRouteBlockTok) {
+    switch (router_nw(m.d)) {
+      case 1: launch_blocks<1>(m, xx, wr, bias, logits, stream); break;
+      case 2: launch_blocks<2>(m, xx, wr, bias, logits, stream); break;
+      default: launch_blocks<4>(m, xx, wr, bias, logits, stream); break;
+    }
+    return;
+  }
   switch (router_nw(m.d)) {
     case 1: launch_router<1>(m, xx, wr, bias, logits, stream); break;
     case 2: launch_router<2>(m, xx, wr, bias, logits, stream); break;

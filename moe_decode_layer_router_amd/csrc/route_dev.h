@@ -149,6 +149,80 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
   }
 }
 
+// Larger S: kRouteBlockTok tokens x NE expert rows a workgroup. Every
+// (token, expert) logit is summed exactly as router_row sums it (per-lane
+// loop, shuffle tree, pairwise tree over the 16 K slices), so the two give
+// the same bits; here each x tile a wave loads serves NE router rows, which
+// cuts the x a workgroup reads from L2 to kRouteBlockTok / S of router_row's.
+constexpr int kRouteBlockTok = 16;
+
+template <int NW, int NE>
+__device__ __forceinline__ void router_block(const uint16_t* __restrict__ x,
+                                             const float* __restrict__ wr,
+                                             const float* __restrict__ bias,
+                                             float* __restrict__ logits, int S, int d, int E,
+                                             int e0, int t0,
+                                             float (*red)[kRouteWaves][kTok]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int kq = d / kRouteWaves;
+  const int nf = kq / 4;
+  const int k0 = w * kq;
+  const int tn = min(kRouteBlockTok, S - t0);
+  int f[NW];
+  bool live[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    live[i] = lane + kWave * i < nf;
+    f[i] = min(lane + kWave * i, nf - 1);
+  }
+  f32x4_t wv[NE][NW];
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    const float* wrow = wr + static_cast<size_t>(min(e0 + j, E - 1)) * d + k0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) wv[j][i] = ld_nt<f32x4_t>(wrow + 4 * f[i]);
+  }
+  const int tok = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+  for (int tile = 0; tile * kTok < tn; ++tile) {
+    uint2 xv[kTok][NW];
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+      const uint16_t* xr = x + static_cast<size_t>(min(t0 + tile * kTok + t, S - 1)) * d + k0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) xv[t][i] = *reinterpret_cast<const uint2*>(xr + 4 * f[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      float acc[kTok];
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) {
+        acc[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+          if (live[i]) acc[t] = dot4(xv[t][i], wv[j][i], acc[t]);
+      }
+      const float v = reduce8(acc, lane);
+      if ((lane & 7) == 0) red[tile * NE + j][w][tok] = v;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < tn * NE; idx += blockDim.x) {
+    const int t = idx / NE, j = idx - t * NE;
+    const int e = e0 + j;
+    if (e >= E) continue;
+    const float(*rt)[kTok] = red[(t / kTok) * NE + j];
+    const int q0 = t % kTok;
+    float q[kRouteWaves / 2];
+#pragma unroll
+    for (int i = 0; i < kRouteWaves / 2; ++i) q[i] = rt[2 * i][q0] + rt[2 * i + 1][q0];
+#pragma unroll
+    for (int i = 0; i < kRouteWaves / 4; ++i) q[i] = q[2 * i] + q[2 * i + 1];
+    const float sum = (q[0] + q[1]) + (q[2] + q[3]);
+    logits[static_cast<size_t>(t0 + t) * E + e] = sum + (bias ? bias[e] : 0.0f);
+  }
+}
+
 // A logit as an unsigned key with the same order; -0 is folded into +0 so
 // that both compare equal. Finite logits never map to 0.
 __device__ __forceinline__ uint32_t order_key(float l) {
