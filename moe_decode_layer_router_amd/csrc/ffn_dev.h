@@ -133,6 +133,9 @@ __device__ __forceinline__ void load_w(MxChunk<TTG>& ch, const uint8_t* wlane, c
   ch.s = ld_nt<uint32_t>(slane + static_cast<size_t>(c) * kMxTileBytes);
 }
 
+// The shared expert's tiles are read once per token group, by tasks placed on
+// one XCD (see the shared task order in ffn.hip): plain loads, so the groups
+// after the first find them in that XCD's L2.
 template <int TTG>
 __device__ __forceinline__ void load_w(BfChunk<TTG>& ch, const uint8_t* wlane, const uint8_t*,
                                        int c) {
@@ -140,7 +143,8 @@ __device__ __forceinline__ void load_w(BfChunk<TTG>& ch, const uint8_t* wlane, c
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ch.w[r][q] = ld_nt<u32x4_t>(t + r * 4096 + q * 1024);
+    for (int q = 0; q < 4; ++q)
+      ch.w[r][q] = *reinterpret_cast<const u32x4_t*>(t + r * 4096 + q * 1024);
 }
 
 template <int TTG>
