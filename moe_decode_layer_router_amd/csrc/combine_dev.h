@@ -22,19 +22,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// workgroup-wide sum (256 threads), every thread gets it; fixed order
-__device__ __forceinline__ double block_sum(double v, double* red) {
-  v = wave_sum_f64(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();  // red is reused across calls
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  double s = red[0];
-#pragma unroll
-  for (int i = 1; i < kCombineThreads / kWave; ++i) s += red[i];
-  return s;
-}
-
 // bf16x8 vectors a thread needs for a row of d: the kernels are instantiated
 // for VPT in {1, 2, 4, 8}
 inline int combine_vpt(int d) {
@@ -42,16 +29,59 @@ inline int combine_vpt(int d) {
   return nvec <= 256 ? 1 : nvec <= 512 ? 2 : nvec <= 1024 ? 4 : 8;
 }
 
-// token t: out[t] = sum over slots s with pick_pos >= 0 of
-//   w[t][s] * y[p] / sqrt(mean(y[p]^2) + eps) * gamma  (+ y[shared_row0 + t])
+// workgroup-wide sums of NB values at once (256 threads, one barrier pair),
+// every thread gets them; fixed order: the wave's butterfly, then the 4 waves
+template <int NB>
+__device__ __forceinline__ void block_sum_n(double (&v)[NB], double (*red)[kCombineThreads / kWave]) {
+#pragma unroll
+  for (int i = 0; i < NB; ++i) v[i] = wave_sum_f64(v[i]);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();  // red is reused across calls
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) red[i][w] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    double s = red[i][0];
+#pragma unroll
+    for (int k = 1; k < kCombineThreads / kWave; ++k) s += red[i][k];
+    v[i] = s;
+  }
+}
+
+// slots of a token whose y rows are loaded together (measured: batching pays
+// at d = 7168, not at d <= 4096)
 template <int VPT>
+constexpr int combine_batch() {
+  return VPT == 4 ? 2 : 1;
+}
+
+// token t: out[t] = sum over slots s with pick_pos >= 0 of
+//   w[t][s] * y[p] / sqrt(mean(y[p]^2) + eps) * gamma  (+ y[shared_row0 + t]).
+// The token's pick positions and weights are loaded first, then the y rows of
+// up to combine_batch() slots at once, whose norms share one block reduction;
+// the weighted sum runs in slot order. kCoh: the y rows were written in the
+// same launch by other workgroups (sc1 loads).
+// red: LDS [8][kCombineThreads / kWave] doubles.
+template <int VPT, bool kCoh = false>
 __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y,
                                               const float* __restrict__ tw,
                                               const int32_t* __restrict__ pick_pos,
                                               const uint16_t* __restrict__ gamma,
                                               float* __restrict__ out, int d, int topk, float eps,
-                                              long shared_row0, int t, double* red) {
+                                              long shared_row0, int t,
+                                              double (*red)[kCombineThreads / kWave]) {
+  constexpr int NB = combine_batch<VPT>();
   const int nvec = d / 8;
+  int pp[8];
+  float wt[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    pp[s] = s < topk ? pick_pos[static_cast<size_t>(t) * topk + s] : -1;
+    wt[s] = s < topk ? tw[static_cast<size_t>(t) * topk + s] : 0.0f;
+  }
   float acc[VPT][8], gam[VPT][8];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -71,37 +101,59 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y,
       }
     }
   }
+  __amdgpu_buffer_rsrc_t yr;
+  if constexpr (kCoh)
+    yr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(y), 0, 0x7fffffff, 0x00020000);
   const double inv_d = 1.0 / static_cast<double>(d);
-  for (int s = 0; s < topk; ++s) {
-    const int p = pick_pos[static_cast<size_t>(t) * topk + s];
-    if (p < 0) continue;
-    float yv[VPT][8];
-    double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int v = threadIdx.x + kCombineThreads * i;
+  for (int s0 = 0; s0 < 8; s0 += NB) {
+    bool any = false;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) yv[i][j] = 0.0f;
-      if (v < nvec) {
-        const uint4 q = *reinterpret_cast<const uint4*>(y + static_cast<size_t>(p) * d + 8 * v);
-        const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+    for (int b = 0; b < NB; ++b) any = any || pp[s0 + b] >= 0;
+    if (!any) continue;  // uniform: every thread holds the same pick positions
+    u32x4_t q[NB][VPT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          yv[i][2 * j] = bf16_lo(qw[j]);
-          yv[i][2 * j + 1] = bf16_hi(qw[j]);
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int v = threadIdx.x + kCombineThreads * i;
+        const int p = pp[s0 + b];
+        q[b][i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (p >= 0 && v < nvec) {
+          if constexpr (kCoh)
+            q[b][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                yr, static_cast<uint32_t>((static_cast<size_t>(p) * d + 8 * v) * 2), 0, kCpolSc1);
+          else
+            q[b][i] = *reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(p) * d + 8 * v);
         }
       }
+    double ss[NB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss += static_cast<double>(yv[i][j]) * yv[i][j];
+    for (int b = 0; b < NB; ++b) {
+      ss[b] = 0.0;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const double lo = bf16_lo(q[b][i][j]), hi = bf16_hi(q[b][i][j]);
+          ss[b] += lo * lo;
+          ss[b] += hi * hi;
+        }
     }
-    ss = block_sum(ss, red);
-    const double r = 1.0 / sqrt(ss * inv_d + static_cast<double>(eps));
-    const float wt = tw[static_cast<size_t>(t) * topk + s];
+    block_sum_n<NB>(ss, red);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
+    for (int b = 0; b < NB; ++b) {
+      if (pp[s0 + b] < 0) continue;
+      const double r = 1.0 / sqrt(ss[b] * inv_d + static_cast<double>(eps));
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j] += wt * (static_cast<float>(yv[i][j] * r) * gam[i][j]);
+      for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][2 * j] += wt[s0 + b] * (static_cast<float>(bf16_lo(q[b][i][j]) * r) * gam[i][2 * j]);
+          acc[i][2 * j + 1] +=
+              wt[s0 + b] * (static_cast<float>(bf16_hi(q[b][i][j]) * r) * gam[i][2 * j + 1]);
+        }
+    }
   }
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
