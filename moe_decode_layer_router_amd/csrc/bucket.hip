@@ -15,8 +15,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(const int32_t* __restrict_
                                                       int topk, int n_loc, int local_base,
                                                       int R_max) {
   __shared__ BucketLds L;
-  bucket_block(ids, S, topk, n_loc, local_base, R_max, L, nullptr, true, counts, offsets, rows,
-               pick_pos, active);
+  bucket_block(ids, S, topk, n_loc, local_base, R_max, L, counts, offsets, rows, pick_pos, active);
 }
 
 }  // namespace

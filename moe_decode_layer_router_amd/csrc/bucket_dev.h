@@ -17,32 +17,32 @@ constexpr int kMaskWords = kMaxTokens / 32;
 
 struct BucketLds {
   uint32_t mask[32][kMaskWords];  // token bitmask of each local expert
-  int32_t cnt[32];                // picks of each local expert
   int32_t off[33];                // bucket offsets (exclusive prefix sums)
-  int32_t nv;                     // local experts with a pick
 };
 
-// All threads of the workgroup call this. Fills L; if rows_lds is given, the
-// token of every bucket row; if `glob`, also the ABI outputs counts, offsets,
-// rows (-1 past the last bucket row, up to R_max), pick_pos and active.
+// The steps, all threads of the workgroup calling each one:
+//   bucket_clear(L); __syncthreads();
+//   bucket_mark(L, el, t) for every local pick (any thread, any order);
+//   __syncthreads(); bucket_finish(...).
+__device__ __forceinline__ void bucket_clear(BucketLds& L) {
+  if (threadIdx.x < 32 * kMaskWords) L.mask[threadIdx.x / kMaskWords][threadIdx.x % kMaskWords] = 0u;
+}
+
+// token t picked local expert el
+__device__ __forceinline__ void bucket_mark(BucketLds& L, int el, int t) {
+  atomicOr(&L.mask[el][t >> 5], 1u << (t & 31));
+}
+
+// From the marks: counts, offsets, active (wave 0), then every pick's bucket
+// row (rows, pick_pos; rows past the last bucket row are -1 up to R_max).
 // A token's ids must be distinct.
-__device__ __forceinline__ void bucket_block(const int32_t* __restrict__ ids, int S, int topk,
-                                             int n_loc, int local_base, int R_max, BucketLds& L,
-                                             int32_t* rows_lds, bool glob, int32_t* counts,
-                                             int32_t* offsets, int32_t* rows, int32_t* pick_pos,
-                                             int32_t* active) {
+__device__ __forceinline__ void bucket_finish(const int32_t* __restrict__ ids, int S, int topk,
+                                              int n_loc, int local_base, int R_max, BucketLds& L,
+                                              int32_t* counts, int32_t* offsets, int32_t* rows,
+                                              int32_t* pick_pos, int32_t* active) {
   const int tid = threadIdx.x;
   const int nth = blockDim.x;
   const int npick = S * topk;
-  if (tid < 32 * kMaskWords) L.mask[tid / kMaskWords][tid % kMaskWords] = 0u;
-  __syncthreads();
-  for (int p = tid; p < npick; p += nth) {
-    const int el = ids[p] - local_base;
-    const int t = p / topk;
-    if (el >= 0 && el < n_loc) atomicOr(&L.mask[el][t >> 5], 1u << (t & 31));
-  }
-  __syncthreads();
-
   // wave 0, lane e: expert e's count, its bucket offset (wave prefix sum) and
   // its slot in the active list (ballot of the experts with picks)
   if (tid < kWave) {
@@ -61,21 +61,17 @@ __device__ __forceinline__ void bucket_block(const int32_t* __restrict__ ids, in
     const uint64_t act = __ballot(e < n_loc && c > 0);
     const int nv = __popcll(act);
     if (e < n_loc) {
-      L.cnt[e] = c;
       L.off[e] = incl - c;
+      counts[e] = c;
+      offsets[e] = incl - c;
+      if (c > 0) active[1 + __popcll(act & ((1ull << e) - 1ull))] = e;
+      if (e >= nv) active[1 + e] = -1;
     }
-    if (e == n_loc - 1) L.off[n_loc] = incl;
-    if (e == 0) L.nv = nv;
-    if (glob) {
-      if (e < n_loc) {
-        counts[e] = c;
-        offsets[e] = incl - c;
-        if (c > 0) active[1 + __popcll(act & ((1ull << e) - 1ull))] = e;
-        if (e >= nv) active[1 + e] = -1;
-      }
-      if (e == n_loc - 1) offsets[n_loc] = incl;
-      if (e == 0) active[0] = nv;
+    if (e == n_loc - 1) {
+      L.off[n_loc] = incl;
+      offsets[n_loc] = incl;
     }
+    if (e == 0) active[0] = nv;
   }
   __syncthreads();
 
@@ -92,14 +88,26 @@ __device__ __forceinline__ void bucket_block(const int32_t* __restrict__ ids, in
         else if (w == (t >> 5)) below += __popc(bits & ((1u << (t & 31)) - 1u));
       }
       pos = L.off[el] + below;
-      if (rows_lds) rows_lds[pos] = t;
-      if (glob) rows[pos] = t;
+      rows[pos] = t;
     }
-    if (glob) pick_pos[p] = pos;
+    pick_pos[p] = pos;
   }
-  if (glob)
-    for (int r = L.off[n_loc] + tid; r < R_max; r += nth) rows[r] = -1;
+  for (int r = L.off[n_loc] + tid; r < R_max; r += nth) rows[r] = -1;
+}
+
+// All of it from ids in memory (the moe_bucket kernel).
+__device__ __forceinline__ void bucket_block(const int32_t* __restrict__ ids, int S, int topk,
+                                             int n_loc, int local_base, int R_max, BucketLds& L,
+                                             int32_t* counts, int32_t* offsets, int32_t* rows,
+                                             int32_t* pick_pos, int32_t* active) {
+  bucket_clear(L);
   __syncthreads();
+  for (int p = threadIdx.x; p < S * topk; p += blockDim.x) {
+    const int el = ids[p] - local_base;
+    if (el >= 0 && el < n_loc) bucket_mark(L, el, p / topk);
+  }
+  __syncthreads();
+  bucket_finish(ids, S, topk, n_loc, local_base, R_max, L, counts, offsets, rows, pick_pos, active);
 }
 
 }  // namespace moeblk

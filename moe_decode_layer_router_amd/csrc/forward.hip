@@ -27,8 +27,9 @@ namespace {
 
 constexpr int kTopkThreads = 1024;
 
-// top-k of every token (wave w takes tokens w, w + 16, ...), then the
-// bucketing of the picks (ids handed over in LDS), in one workgroup
+// top-k of every token (wave w takes tokens w, w + 16, ...), marking the
+// local picks as they are found, then the bucketing (ids handed over in LDS),
+// in one workgroup
 __global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
     const float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ rows,
@@ -36,12 +37,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
     int renorm, int n_loc, int local_base, int R_max) {
   __shared__ BucketLds L;
   __shared__ int32_t ids_l[kMaxTokens * 8];
-  const int wv = threadIdx.x >> 6;
-  for (int t = wv; t < S; t += kTopkThreads / kWave)
-    topk_token(logits, ids, w, ids_l, E, topk, renorm, t);
+  bucket_clear(L);
   __syncthreads();
-  bucket_block(ids_l, S, topk, n_loc, local_base, R_max, L, nullptr, true, counts, offsets, rows,
-               pick_pos, active);
+  const int wv = threadIdx.x >> 6;
+  auto mark = [&](int id, int t) {
+    const int el = id - local_base;
+    if (el >= 0 && el < n_loc) bucket_mark(L, el, t);
+  };
+  for (int t = wv; t < S; t += kTopkThreads / kWave)
+    topk_token(logits, ids, w, ids_l, E, topk, renorm, t, mark);
+  __syncthreads();
+  bucket_finish(ids_l, S, topk, n_loc, local_base, R_max, L, counts, offsets, rows, pick_pos,
+                active);
 }
 
 }  // namespace

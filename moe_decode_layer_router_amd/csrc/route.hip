@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int topk, int renorm) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= S) return;
-  topk_token(logits, ids, w, nullptr, E, topk, renorm, t);
+  topk_token(logits, ids, w, nullptr, E, topk, renorm, t, NoMark{});
 }
 
 template <int NW>

@@ -250,6 +250,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // (ka, ia) ranks before (kb, ib): larger key, or equal key and lower id
+struct NoMark {
+  __device__ void operator()(int, int) const {}
+};
+
 __device__ __forceinline__ bool ranks_before(uint32_t ka, int ia, uint32_t kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
@@ -274,10 +278,13 @@ __device__ __forceinline__ void order2(uint32_t& ka, int& ia, uint32_t& kb, int&
 //    drops its first entry.
 // 3. Lane s < k holds slot s: sigmoid score, renormalised by the sum of the k
 //    scores in slot order.
-// ids_lds: if not NULL, the ids are also written there ([t * topk + slot]).
+// ids_lds: if not NULL, the ids are also written there ([t * topk + slot]);
+// mark(id, t) runs for each of the token's ids (lanes < topk).
+template <class Mark>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
-                                           int32_t* ids_lds, int E, int topk, int renorm, int t) {
+                                           int32_t* ids_lds, int E, int topk, int renorm, int t,
+                                           Mark mark) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t k[4];
   int id[4];
@@ -334,6 +341,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
   if (lane < topk) {
     ids[static_cast<size_t>(t) * topk + lane] = my_id;
     if (ids_lds) ids_lds[t * topk + lane] = my_id;
+    mark(my_id, t);
     w[static_cast<size_t>(t) * topk + lane] = renorm ? sc / sum : sc;
   }
 }
