@@ -115,6 +115,41 @@ def test_deterministic():
         assert np.array_equal(g1[k], g2[k]), k
 
 
+def _random_dims(seed):
+    """Seeded random problem sizes inside the supported ranges (small d and I,
+    so the oracle stays quick)."""
+    r = np.random.default_rng([seed, 77])
+    E = int(r.integers(1, 65))
+    topk = int(r.integers(1, min(8, E) + 1))
+    n_local = int(r.integers(1, min(32, E) + 1))
+    return dict(
+        S=int(r.integers(1, 129)),
+        d=128 * int(r.integers(1, 9)),
+        E=E,
+        topk=topk,
+        n_local=n_local,
+        local_base=int(r.integers(0, E - n_local + 1)),
+        I=128 * int(r.integers(1, 5)),
+        renorm=int(r.integers(0, 2)),
+        shared_I=[0, 0, 128, 256][int(r.integers(0, 4))],
+        bias_kind=["none", "local"][int(r.integers(0, 2))],
+        beta=float(r.uniform(-0.5, 0.5)),
+    )
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    """Random sizes within the supported ranges: the four calls against the
+    oracle, and moe_forward against the four calls bit for bit."""
+    kw = _random_dims(seed)
+    inp = make_inputs(_tiny(**kw), 100 + seed, gamma="random")
+    g = run_gpu(inp)
+    check_block(inp, g, strict=False)
+    g1 = run_gpu(inp, g["blk"], fused=True)
+    for k in ("logits", "ids", "w", "counts", "offsets", "rows", "pick_pos", "active", "out"):
+        assert np.array_equal(g1[k], g[k]), (k, kw)
+
+
 # ------------------------------------------------------------ full workloads
 
 
