@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOEBLK_ABI_VERSION 1
+#define MOEBLK_ABI_VERSION 2 /* 2: moe_dims.bias_mode */
 
 /* status codes */
 #define MOE_OK 0
@@ -68,7 +68,8 @@ extern "C" {
  *   1 <= topk <= 8, topk <= E; 1 <= n_local <= 32;
  *   0 <= local_base, local_base + n_local <= E;
  *   128 <= I <= 8192, I % 128 == 0; renorm in {0, 1}; eps finite, >= 0;
- *   shared_I == 0 or (128 <= shared_I <= 8192, shared_I % 128 == 0). */
+ *   shared_I == 0 or (128 <= shared_I <= 8192, shared_I % 128 == 0);
+ *   bias_mode in {0, 1}. */
 typedef struct moe_dims {
   int32_t S;          /* token rows */
   int32_t d;          /* hidden size seen by the experts */
@@ -80,6 +81,10 @@ typedef struct moe_dims {
   int32_t renorm;     /* 1: w = sigmoid / sum of the token's topk sigmoids; 0: w = sigmoid */
   float eps;          /* post-expert RMSNorm epsilon */
   int32_t shared_I;   /* 0: no shared expert; else its intermediate size */
+  int32_t bias_mode;  /* router bias: 0 part of the logit (ranking and sigmoid);
+                         1 selection only (ranking key logit + bias, sigmoid of
+                         the unbiased logit). The K3 page's "route_token"
+                         summary breaks off after "sigmoid +", allowing both */
 } moe_dims;
 
 /* R_max = S * min(topk, n_local): the most local picks a call can have
@@ -127,12 +132,14 @@ int moe_pack_bf16(const moe_dims* dims, int which, const void* w, void* packed,
 
 /* Router logits and top-k (K3 page stages "A" and "route"; K5 page, HA).
  *   x        [S, d] bf16 activations;
- *   w_router [E, d] fp32; bias [E] fp32 or NULL (added to the logit, before
- *            ranking and sigmoid);
- *   logits   [S, E] fp32, written: sum_j x[t][j] w_router[e][j] (+ bias[e]),
- *            fp32 accumulation;
- *   topk_ids [S, topk] int32, written: the token's experts by descending
- *            logit, equal logits to the lower id;
+ *   w_router [E, d] fp32; bias [E] fp32 or NULL (bias_mode 0: added to the
+ *            logit, before ranking and sigmoid; 1: added to the ranking key
+ *            only);
+ *   logits   [S, E] fp32, written: sum_j x[t][j] w_router[e][j], fp32
+ *            accumulation, + bias[e] under bias_mode 0;
+ *   topk_ids [S, topk] int32, written: the token's experts by descending key,
+ *            equal keys to the lower id; the key is the logit, or under
+ *            bias_mode 1 the fp32 sum logit + bias[e];
  *   topk_w   [S, topk] fp32, written: sigmoid(logit), divided by the sum over
  *            the token's topk picks when renorm = 1. */
 int moe_route(const moe_dims* dims, const void* x, const float* w_router, const float* bias,

@@ -48,6 +48,10 @@ MOE_W13 = 0
 MOE_W2 = 1
 
 
+# the layout of moe_dims and the entry points below (MOEBLK_ABI_VERSION)
+ABI_VERSION = 2
+
+
 class MoeDims(ctypes.Structure):
     _fields_ = [
         ("S", ctypes.c_int32),
@@ -60,6 +64,7 @@ class MoeDims(ctypes.Structure):
         ("renorm", ctypes.c_int32),
         ("eps", ctypes.c_float),
         ("shared_I", ctypes.c_int32),
+        ("bias_mode", ctypes.c_int32),
     ]
 
     @property
@@ -89,6 +94,11 @@ def lib() -> ctypes.CDLL:
             )
         L = ctypes.CDLL(_LIB_PATH)
         L.moe_abi_version.restype = ctypes.c_int
+        if L.moe_abi_version() != ABI_VERSION:
+            raise RuntimeError(
+                f"{_LIB_PATH} has ABI version {L.moe_abi_version()}, this binding expects "
+                f"{ABI_VERSION}: rebuild it"
+            )
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_check_dims.argtypes = [_DP]
@@ -118,11 +128,11 @@ def lib() -> ctypes.CDLL:
 
 def dims_from(cfg) -> MoeDims:
     """MoeDims from an object or dict with the moe_dims field names."""
-    get = cfg.get if isinstance(cfg, dict) else (lambda k, _=None: getattr(cfg, k))
+    get = cfg.get if isinstance(cfg, dict) else (lambda k, dflt=None: getattr(cfg, k, dflt))
     return MoeDims(
         S=get("S"), d=get("d"), E=get("E"), topk=get("topk"), n_local=get("n_local"),
         local_base=get("local_base"), I=get("I"), renorm=get("renorm"), eps=get("eps"),
-        shared_I=get("shared_I"),
+        shared_I=get("shared_I"), bias_mode=get("bias_mode", 0),
     )
 
 

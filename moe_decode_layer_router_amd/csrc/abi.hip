@@ -18,6 +18,7 @@ int check_dims(const moe_dims* d) {
                   (d->shared_I >= 128 && d->shared_I <= 8192 && d->shared_I % 128 == 0),
               MOE_ERR_SHAPE);
   MOE_REQUIRE(d->renorm == 0 || d->renorm == 1, MOE_ERR_UNSUPPORTED);
+  MOE_REQUIRE(d->bias_mode == 0 || d->bias_mode == 1, MOE_ERR_UNSUPPORTED);
   MOE_REQUIRE(isfinite(d->eps) && d->eps >= 0.0f, MOE_ERR_UNSUPPORTED);
   return MOE_OK;
 }

@@ -31,8 +31,8 @@ constexpr int kTopkThreads = 1024;
 // local picks as they are found, then the bucketing (ids handed over in LDS),
 // in one workgroup
 __global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
-    const float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ rows,
+    const float* __restrict__ logits, const float* __restrict__ sel_bias,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ rows,
     int32_t* __restrict__ pick_pos, int32_t* __restrict__ active, int S, int E, int topk,
     int renorm, int n_loc, int local_base, int R_max) {
   __shared__ BucketLds L;
@@ -44,8 +44,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
     const int el = id - local_base;
     if (el >= 0 && el < n_loc) bucket_mark(L, el, t);
   };
-  for (int t = wv; t < S; t += kTopkThreads / kWave)
-    topk_token(logits, ids, w, ids_l, E, topk, renorm, t, mark);
+  if (sel_bias) {
+    for (int t = wv; t < S; t += kTopkThreads / kWave)
+      topk_token<true>(logits, sel_bias, ids, w, ids_l, E, topk, renorm, t, mark);
+  } else {
+    for (int t = wv; t < S; t += kTopkThreads / kWave)
+      topk_token<false>(logits, nullptr, ids, w, ids_l, E, topk, renorm, t, mark);
+  }
   __syncthreads();
   bucket_finish(ids_l, S, topk, n_loc, local_base, R_max, L, counts, offsets, rows, pick_pos,
                 active);
@@ -87,11 +92,11 @@ extern "C" int moe_forward(const moe_dims* dims, const void* x, const float* w_r
 
   launch_router_logits(m, x, w_router, bias, logits, stream);
   if (m.S <= kTopkThreads / kWave) {
-    hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits, topk_ids,
-                       topk_w, counts, offsets, rows, pick_pos, active, m.S, m.E, m.topk, m.renorm,
+    hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits,
+                       select_bias(m, bias), topk_ids, topk_w, counts, offsets, rows, pick_pos, active, m.S, m.E, m.topk, m.renorm,
                        m.n_local, m.local_base, r_max(m));
   } else {  // a wave a token needs more waves than one workgroup holds
-    launch_topk(m, logits, topk_ids, topk_w, stream);
+    launch_topk(m, logits, bias, topk_ids, topk_w, stream);
     launch_bucket(m, topk_ids, counts, offsets, rows, pick_pos, active, stream);
   }
   const int frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y,

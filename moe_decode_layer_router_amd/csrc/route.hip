@@ -50,13 +50,16 @@ void launch_blocks(const moe_dims& m, const uint16_t* x, const float* wr, const 
 }
 
 // one wave per token
+// (sel_bias: the selection-only bias, or NULL)
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                   const float* __restrict__ sel_bias,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w, int S, int E,
                                                    int topk, int renorm) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= S) return;
-  topk_token(logits, ids, w, nullptr, E, topk, renorm, t, NoMark{});
+  if (sel_bias) topk_token<true>(logits, sel_bias, ids, w, nullptr, E, topk, renorm, t, NoMark{});
+  else topk_token<false>(logits, nullptr, ids, w, nullptr, E, topk, renorm, t, NoMark{});
 }
 
 template <int NW>
@@ -70,6 +73,7 @@ void launch_router(const moe_dims& m, const uint16_t* x, const float* wr, const 
 
 void launch_router_logits(const moe_dims& m, const void* x, const float* wr, const float* bias,
                           float* logits, hipStream_t stream) {
+  bias = logit_bias(m, bias);
   const uint16_t* xx = static_cast<const uint16_t*>(x);
   if (m.S > kRouteBlockTok) {
     switch (router_nw(m.d)) {
@@ -86,9 +90,10 @@ void launch_router_logits(const moe_dims& m, const void* x, const float* wr, con
   }
 }
 
-void launch_topk(const moe_dims& m, const float* logits, int32_t* ids, float* w, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_kernel, dim3((m.S + 3) / 4), dim3(256), 0, stream, logits, ids, w, m.S,
-                     m.E, m.topk, m.renorm);
+void launch_topk(const moe_dims& m, const float* logits, const float* bias, int32_t* ids, float* w,
+                 hipStream_t stream) {
+  hipLaunchKernelGGL(topk_kernel, dim3((m.S + 3) / 4), dim3(256), 0, stream, logits,
+                     select_bias(m, bias), ids, w, m.S, m.E, m.topk, m.renorm);
 }
 
 }  // namespace moeblk
@@ -105,6 +110,6 @@ extern "C" int moe_route(const moe_dims* dims, const void* x, const float* w_rou
                   aligned16(topk_w) && (!bias || aligned16(bias)),
               MOE_ERR_ALIGN);
   launch_router_logits(*dims, x, w_router, bias, logits, stream);
-  launch_topk(*dims, logits, topk_ids, topk_w, stream);
+  launch_topk(*dims, logits, bias, topk_ids, topk_w, stream);
   return launch_status();
 }

@@ -3,9 +3,11 @@
 //
 // Muse Spark K3 page, stage "A": router logits in fp32; stage "route": every
 // token's top-8, identical wherever computed. K5 page, HA routing tail: top-8
-// per token, ids and weights handed to the expert launch. The bias is added to
-// the logit before ranking (Kimi-K3 layer page, "k2_launch": router weight and
-// bias).
+// per token, ids and weights handed to the expert launch. The router bias
+// (Kimi-K3 layer page, "k2_launch": router weight and bias) is either part of
+// the logit, before ranking and sigmoid, or (selection-only) added to the
+// ranking key alone while the sigmoid takes the unbiased logit: the K3 page's
+// summary of "route_token" breaks off after "sigmoid +", which allows both.
 #pragma once
 
 #include "common.h"
@@ -269,6 +271,17 @@ __device__ __forceinline__ void order2(uint32_t& ka, int& ia, uint32_t& kb, int&
   }
 }
 
+// order2 that also carries a value with each key
+__device__ __forceinline__ void order2(uint32_t& ka, int& ia, float& la, uint32_t& kb, int& ib,
+                                       float& lb) {
+  if (ranks_before(kb, ib, ka, ia)) {
+    const float l = la;
+    la = lb;
+    lb = l;
+  }
+  order2(ka, ia, kb, ib);
+}
+
 // Wave-level: the top-k of token t; lane l holds experts l, l + 64, l + 128,
 // l + 192 (E <= 256).
 // 1. Each lane orders its 4 experts (larger logit first, equal logits lower id
@@ -278,31 +291,47 @@ __device__ __forceinline__ void order2(uint32_t& ka, int& ia, uint32_t& kb, int&
 //    drops its first entry.
 // 3. Lane s < k holds slot s: sigmoid score, renormalised by the sum of the k
 //    scores in slot order.
+// kSel (selection-only bias): the key is fl(logit + sel_bias[e]) and the
+// sigmoid takes the unbiased logit, which travels with its key through the
+// ordering.
 // ids_lds: if not NULL, the ids are also written there ([t * topk + slot]);
 // mark(id, t) runs for each of the token's ids (lanes < topk).
-template <class Mark>
+template <bool kSel, class Mark>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
+                                           const float* __restrict__ sel_bias,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
                                            int32_t* ids_lds, int E, int topk, int renorm, int t,
                                            Mark mark) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t k[4];
   int id[4];
+  float lg[4];  // kSel: the unbiased logits
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + kWave * j;
     const float* p = logits + static_cast<size_t>(t) * E + e;
-    k[j] = e < E ? order_key(*p) : 0u;  // 0: below every expert
+    lg[j] = e < E ? *p : 0.0f;
+    if constexpr (kSel) k[j] = e < E ? order_key(lg[j] + sel_bias[e]) : 0u;
+    else k[j] = e < E ? order_key(lg[j]) : 0u;  // 0: below every expert
     id[j] = e;
   }
-  order2(k[0], id[0], k[1], id[1]);
-  order2(k[2], id[2], k[3], id[3]);
-  order2(k[0], id[0], k[2], id[2]);
-  order2(k[1], id[1], k[3], id[3]);
-  order2(k[1], id[1], k[2], id[2]);
+  if constexpr (kSel) {
+    order2(k[0], id[0], lg[0], k[1], id[1], lg[1]);
+    order2(k[2], id[2], lg[2], k[3], id[3], lg[3]);
+    order2(k[0], id[0], lg[0], k[2], id[2], lg[2]);
+    order2(k[1], id[1], lg[1], k[3], id[3], lg[3]);
+    order2(k[1], id[1], lg[1], k[2], id[2], lg[2]);
+  } else {
+    order2(k[0], id[0], k[1], id[1]);
+    order2(k[2], id[2], k[3], id[3]);
+    order2(k[0], id[0], k[2], id[2]);
+    order2(k[1], id[1], k[3], id[3]);
+    order2(k[1], id[1], k[2], id[2]);
+  }
 
   uint32_t my_key = 0;
   int my_id = 0;
+  float my_lg = 0.0f;
   for (int r = 0; r < topk; ++r) {
     const uint32_t m = wave_max_u32(k[0]);
     const uint64_t tie = __ballot(k[0] == m);
@@ -320,6 +349,10 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
         }
       }
     }
+    if constexpr (kSel) {
+      const float wlg = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lg[0]), wl));
+      if (lane == r) my_lg = wlg;
+    }
     if (lane == r) {
       my_key = m;
       my_id = wid;
@@ -332,9 +365,15 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
       k[2] = k[3];
       id[2] = id[3];
       k[3] = 0u;
+      if constexpr (kSel) {
+        lg[0] = lg[1];
+        lg[1] = lg[2];
+        lg[2] = lg[3];
+      }
     }
   }
-  const float sc = 1.0f / (1.0f + expf(-key_logit(my_key)));
+  const float l = kSel ? my_lg : key_logit(my_key);
+  const float sc = 1.0f / (1.0f + expf(-l));
   float sum = 0.0f;
   for (int q = 0; q < topk; ++q)
     sum += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sc), q));

@@ -60,11 +60,13 @@ def _declare(L):
     L.orc_expert_ffn.argtypes = [_I] * 6 + [_P] * 11
     L.orc_norm_row.argtypes = [_I, _P, _P, _D, _P]
     L.orc_combine.argtypes = [_I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P]
-    L.orc_forward.argtypes = [_I] * 8 + [_F, _I] + [_P] * 20
+    L.orc_topk_sel.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
+    L.orc_forward.argtypes = [_I] * 8 + [_F, _I, _I] + [_P] * 20
     for f in (
         "orc_router_logits",
         "orc_route_weights",
         "orc_topk",
+        "orc_topk_sel",
         "orc_bucket",
         "orc_expert_row",
         "orc_shared_row",
@@ -151,6 +153,17 @@ def topk(logits, k, renorm=1):
     ids = np.empty((S, k), np.int32)
     w = np.empty((S, k), np.float32)
     _chk(lib().orc_topk(S, E, int(k), int(renorm), _ptr(logits), _ptr(ids), _ptr(w)), "topk")
+    return ids, w
+
+
+def topk_sel(logits, bias, k, renorm=1):
+    """Selection-only bias: top-k of logits + bias, weights from the logits."""
+    logits = _c(logits, np.float64)
+    bias = _c(bias, np.float32)
+    S, E = logits.shape
+    ids = np.empty((S, k), np.int32)
+    w = np.empty((S, k), np.float32)
+    _chk(lib().orc_topk_sel(S, E, int(k), int(renorm), _ptr(logits), _ptr(bias), _ptr(ids), _ptr(w)), "topk_sel")
     return ids, w
 
 
@@ -321,7 +334,7 @@ def forward(inp: dict) -> dict:
     outs = [logits, ids, w, counts, offsets, rows, pick_pos, active, y, out]
     _chk(
         lib().orc_forward(
-            S, d, E, k, n, cfg.local_base, I, cfg.renorm, float(cfg.eps), Is,
+            S, d, E, k, n, cfg.local_base, I, cfg.renorm, float(cfg.eps), Is, int(cfg.bias_mode),
             *[_ptr(a) for a in ins], *[_ptr(a) for a in outs],
         ),
         "forward",

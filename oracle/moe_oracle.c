@@ -29,7 +29,11 @@
  *
  * Readings where the pages are silent (each one is a choice, listed with its
  * reason in the design notes):
- *   - the router bias is added to the logit before ranking and sigmoid;
+ *   - the router bias is added to the logit before ranking and sigmoid
+ *     (bias_mode 0); the K3 page's one-line summary of "route_token" breaks
+ *     off after "sigmoid +", so the other reading, a bias that steers the selection only
+ *     while the weights come from the sigmoid of the unbiased logit, is kept
+ *     as bias_mode 1 (orc_topk_sel);
  *   - equal logits: the lower expert id ranks first;
  *   - renormalisation is over all k picks, local or not;
  *   - rows [0, I) of gate_up are the gate, rows [I, 2I) the up projection;
@@ -171,6 +175,23 @@ int orc_topk(int S, int E, int topk, int renorm, const double* logits, int32_t* 
     }
   }
   return w ? orc_route_weights(S, E, topk, renorm, logits, ids, w) : ORC_OK;
+}
+
+/* Selection-only bias (bias_mode 1): the picks are the top-k of the scores
+ * logits + bias (fp64, equal scores to the lower id), the weights are the
+ * sigmoids of the unbiased logits of those picks. */
+int orc_topk_sel(int S, int E, int topk, int renorm, const double* logits, const float* bias,
+                 int32_t* ids, float* w) {
+  if (S < 0 || E <= 0 || E > 4096 || topk <= 0 || topk > E || !logits || !bias || !ids)
+    return ORC_EINVAL;
+  double* score = (double*)malloc(sizeof(double) * ((size_t)S * E + 1));
+  if (!score) return ORC_EINVAL;
+  for (int t = 0; t < S; ++t)
+    for (int e = 0; e < E; ++e) score[(long)t * E + e] = logits[(long)t * E + e] + (double)bias[e];
+  int rc = orc_topk(S, E, topk, renorm, score, ids, NULL);
+  free(score);
+  if (rc || !w) return rc;
+  return orc_route_weights(S, E, topk, renorm, logits, ids, w);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -416,18 +437,25 @@ int orc_combine(int S, int d, int topk, int n_loc, int Is, float eps, const uint
 /* ------------------------------------------------------------------------ */
 
 /* route -> bucket -> expert FFN -> combine, all outputs caller-owned:
+ * bias_mode 0: the bias is part of the logit; 1: it steers the selection only
+ * (logits are then written without it);
  * logits [S][E] fp64, ids/w [S][topk], counts [n_loc], offsets [n_loc+1],
  * rows [R_max], pick_pos [S][topk], active [1+n_loc], y [R_max (+S)][d],
  * out [S][d]. */
 int orc_forward(int S, int d, int E, int topk, int n_loc, int local_base, int I, int renorm,
-                float eps, int Is, const uint16_t* x, const float* wr, const float* bias,
+                float eps, int Is, int bias_mode, const uint16_t* x, const float* wr,
+                const float* bias,
                 const uint8_t* w13q, const uint8_t* w13s, const uint8_t* w2q,
                 const uint8_t* w2s, const uint16_t* gamma, const uint16_t* ws13,
                 const uint16_t* ws2, double* logits, int32_t* ids, float* w, int32_t* counts,
                 int32_t* offsets, int32_t* rows, int32_t* pick_pos, int32_t* active,
                 uint16_t* y, float* out) {
-  int rc = orc_router_logits(S, d, E, x, wr, bias, logits);
-  if (!rc) rc = orc_topk(S, E, topk, renorm, logits, ids, w);
+  if (bias_mode != 0 && bias_mode != 1) return ORC_EINVAL;
+  const int sel = bias_mode == 1 && bias;
+  int rc = orc_router_logits(S, d, E, x, wr, sel ? NULL : bias, logits);
+  if (!rc)
+    rc = sel ? orc_topk_sel(S, E, topk, renorm, logits, bias, ids, w)
+             : orc_topk(S, E, topk, renorm, logits, ids, w);
   if (!rc) rc = orc_bucket(S, topk, n_loc, local_base, ids, counts, offsets, rows, pick_pos, active);
   if (!rc)
     rc = orc_expert_ffn(S, d, I, n_loc, topk, Is, x, w13q, w13s, w2q, w2s, counts, offsets,

@@ -35,6 +35,7 @@ class MoeConfig:
     renorm: int = 1  # routing weights renormalised over the top-k
     eps: float = 1e-6  # post-expert RMSNorm epsilon
     bias_kind: str = "none"
+    bias_mode: int = 0  # 0: bias in the logit; 1: the bias steers the selection only
     beta: float = 0.0  # "local" bias value
     zipf_s: float = 0.0  # "zipf" exponent
     x_std: float = 1.0
@@ -56,6 +57,7 @@ class MoeConfig:
             renorm=self.renorm,
             eps=self.eps,
             shared_I=self.shared_I,
+            bias_mode=self.bias_mode,
         )
 
     def with_(self, **kw) -> "MoeConfig":

@@ -84,17 +84,22 @@ def dense_block(inp: dict, ids: np.ndarray | None = None) -> dict:
     """Brute force over every (token, local expert) pair, masked by routing.
 
     Routing: fp64 logits by matmul, order by a stable argsort of -logits; the
-    weights through mpmath's sigmoid. ``ids`` overrides the routing choice."""
+    weights through mpmath's sigmoid. With ``bias_mode`` 1 the bias enters the
+    sort key only and the weights use the unbiased logits. ``ids`` overrides
+    the routing choice."""
     import mpmath
 
     cfg = inp["cfg"]
     S, d, E, k, n, I = cfg.S, cfg.d, cfg.E, cfg.topk, cfg.n_local, cfg.I  # noqa: E741
     x = bf16_val(inp["x"])
     logits = x @ inp["wr"].astype(np.float64).T
+    key = logits
     if inp.get("bias") is not None:
-        logits = logits + inp["bias"].astype(np.float64)
+        key = logits + inp["bias"].astype(np.float64)
+        if cfg.bias_mode == 0:
+            logits = key
     if ids is None:
-        ids = np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32)
+        ids = np.argsort(-key, axis=1, kind="stable")[:, :k].astype(np.int32)
     mpmath.mp.dps = 50
     w = np.zeros((S, k), np.float32)
     for t in range(S):

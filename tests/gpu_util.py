@@ -7,9 +7,9 @@ Tolerances (derived from the arithmetic; every comparison states its own):
   where n bounds the roundings on any path of the GPU's summation tree: a
   per-lane loop of at most d / 256 terms, a 6-level shuffle tree, 4 levels
   over the 16 K slices and the bias add, n = d / 256 + 12;
-* top-k: ids bit-exact, except where the oracle's logits of the two
-  experts that trade places differ by < 1e-5 (several answers are then
-  correct); weights within 1e-6 relative of the oracle's weights computed
+* top-k: ids bit-exact, except where the oracle's ranking keys (the logits,
+  or logit + bias under the selection-only bias) of the two experts that
+  trade places differ by < 1e-5 (several answers are then correct); weights within 1e-6 relative of the oracle's weights computed
   from the GPU's own logits;
 * buckets: bit-exact;
 * expert FFN, step by step: the GPU's SwiGLU rows h against the oracle's
@@ -60,7 +60,7 @@ def run_gpu(inp: dict, blk: MoeBlock | None = None, fused: bool = False) -> dict
 def check_logits(inp, g) -> np.ndarray:
     """GPU fp32 logits against the fp64 oracle; returns the oracle's logits."""
     cfg = inp["cfg"]
-    lo = oracle.router_logits(inp["x"], inp["wr"], inp.get("bias"))
+    lo = oracle.router_logits(inp["x"], inp["wr"], inp.get("bias") if cfg.bias_mode == 0 else None)
     mag = np.abs(bf16_val(inp["x"])) @ np.abs(inp["wr"].astype(np.float64)).T
     u = 2.0**-24
     n = cfg.d / 256 + 12
@@ -71,16 +71,23 @@ def check_logits(inp, g) -> np.ndarray:
 
 
 def check_topk(inp, g, lo) -> None:
-    """ids against the oracle's top-k (near-ties excepted), weights against the
-    oracle's weights of the GPU's logits and ids."""
+    """ids against the oracle's top-k (near-ties of the ranking key excepted),
+    weights against the oracle's weights of the GPU's logits and ids. With the
+    selection-only bias the key is logit + bias and the logits are unbiased."""
     cfg = inp["cfg"]
-    ids_o, _ = oracle.topk(lo, cfg.topk, cfg.renorm)
+    bias = inp.get("bias")
+    if cfg.bias_mode == 1 and bias is not None:
+        ids_o, _ = oracle.topk_sel(lo, bias, cfg.topk, cfg.renorm)
+        key = lo + bias.astype(np.float64)
+    else:
+        ids_o, _ = oracle.topk(lo, cfg.topk, cfg.renorm)
+        key = lo
     ids_g = g["ids"]
     for t in range(cfg.S):
         if np.array_equal(ids_o[t], ids_g[t]):
             continue
-        gap = np.abs(lo[t, ids_o[t]] - lo[t, ids_g[t]])
-        assert np.all(gap < 1e-5), f"token {t}: ids {ids_g[t]} vs oracle {ids_o[t]} (logit gaps {gap})"
+        gap = np.abs(key[t, ids_o[t]] - key[t, ids_g[t]])
+        assert np.all(gap < 1e-5), f"token {t}: ids {ids_g[t]} vs oracle {ids_o[t]} (key gaps {gap})"
         assert len(set(ids_g[t])) == cfg.topk
     w_ref = oracle.route_weights(g["logits"].astype(np.float64), ids_g, cfg.renorm)
     np.testing.assert_allclose(g["w"], w_ref, rtol=1e-6, atol=0)

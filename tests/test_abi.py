@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert mb.moe_abi_version() == 1
+    assert mb.moe_abi_version() == mb.ABI_VERSION == 2
     for code in range(-6, 1):
         s = mb.moe_status_string(code)
         assert s and s != "unknown status"
@@ -70,6 +70,8 @@ def test_workload_dims_are_valid(name):
         (dict(I=0), mb.MOE_ERR_SHAPE),
         (dict(shared_I=64), mb.MOE_ERR_SHAPE),
         (dict(renorm=2), mb.MOE_ERR_UNSUPPORTED),
+        (dict(bias_mode=2), mb.MOE_ERR_UNSUPPORTED),
+        (dict(bias_mode=-1), mb.MOE_ERR_UNSUPPORTED),
         (dict(eps=-1.0), mb.MOE_ERR_UNSUPPORTED),
         (dict(eps=float("nan")), mb.MOE_ERR_UNSUPPORTED),
         (dict(S=1, topk=1, n_local=1, E=1, I=128, d=128), mb.MOE_OK),

@@ -89,6 +89,10 @@ EDGE = {
     "zipf": _tiny(S=48, E=64, n_local=8, local_base=8, topk=8, bias_kind="zipf", zipf_s=1.1),
     "d_max16384": _tiny(S=4, d=16384, I=128),
     "d7168_S33": _tiny(S=33, d=7168, I=128, E=32, n_local=8, topk=8),
+    "sel_bias_zipf": _tiny(S=48, E=64, n_local=8, local_base=8, topk=8, bias_kind="zipf", zipf_s=1.1,
+                           bias_mode=1),
+    "sel_bias_strong": _tiny(S=24, E=16, n_local=4, local_base=4, topk=4, bias_kind="local", beta=3.0,
+                             bias_mode=1),
 }
 
 
@@ -134,6 +138,7 @@ def _random_dims(seed):
         shared_I=[0, 0, 128, 256][int(r.integers(0, 4))],
         bias_kind=["none", "local"][int(r.integers(0, 2))],
         beta=float(r.uniform(-0.5, 0.5)),
+        bias_mode=int(r.integers(0, 2)),
     )
 
 
@@ -206,6 +211,8 @@ FUSED = {
     "S1": _tiny(S=1),
     "some_local": _tiny(S=16, E=32, n_local=4, local_base=8, topk=2),
     "d4096_S16": _tiny(S=16, d=4096, I=256, E=16, n_local=8, topk=4),
+    "sel_bias_S16": _tiny(S=16, E=32, n_local=8, topk=4, bias_kind="local", beta=0.5, bias_mode=1),
+    "sel_bias_S40": _tiny(S=40, E=64, n_local=8, topk=6, bias_kind="zipf", zipf_s=1.1, bias_mode=1),
 }
 
 KEYS = ("logits", "ids", "w", "counts", "offsets", "rows", "pick_pos", "active", "out")
@@ -236,6 +243,19 @@ def test_fused_equals_four_calls(name):
 )
 def test_fused_full_workload(name, n_tok):
     cfg = get_config(name)
+    inp = make_inputs(cfg, 0, gamma="random")
+    g1 = run_gpu(inp, fused=True)
+    check_block(inp, g1, tokens=_sample_tokens(g1, cfg, n_tok), strict=True)
+    g4 = run_gpu(inp, g1["blk"])
+    for k in KEYS:
+        assert np.array_equal(g1[k], g4[k]), k
+
+
+@pytest.mark.parametrize("name,n_tok", [("s16_local25", 4), ("s64_zipf", 3)])
+def test_selection_bias_workload(name, n_tok):
+    """The biased workloads with the bias steering the selection only (the
+    other reading of the router bias), through both entry points."""
+    cfg = get_config(name).with_(bias_mode=1)
     inp = make_inputs(cfg, 0, gamma="random")
     g1 = run_gpu(inp, fused=True)
     check_block(inp, g1, tokens=_sample_tokens(g1, cfg, n_tok), strict=True)

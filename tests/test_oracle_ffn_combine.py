@@ -45,11 +45,14 @@ def test_tiny_block_equals_dense_brute_force(seed, gamma):
         dict(S=5, E=12, n_local=3, local_base=3, topk=4, bias_kind="local", beta=0.3),
         dict(S=4, E=8, n_local=8, topk=2, shared_I=128),
         dict(S=7, E=16, n_local=4, local_base=12, topk=2, shared_I=256),
+        dict(S=6, E=16, n_local=8, topk=4, bias_kind="local", beta=0.3, bias_mode=1),
+        dict(S=8, E=32, n_local=8, local_base=8, topk=3, bias_kind="zipf", zipf_s=1.1, bias_mode=1),
     ],
 )
 def test_block_equals_dense_brute_force_general(kw):
-    """Non-local picks, a local range not at 0, renorm off, a routing bias and
-    the shared expert, against the independent dense evaluation."""
+    """Non-local picks, a local range not at 0, renorm off, a routing bias (in
+    the logit, or steering the selection only) and the shared expert, against
+    the independent dense evaluation."""
     cfg = get_config("tiny").with_(**kw)
     inp = make_inputs(cfg, 4, gamma="random")
     got = oracle.forward(inp)

@@ -4,6 +4,8 @@ Logits against numpy's fp64 matmul; top-k against a stable full sort; weights
 against mpmath's sigmoid; ties and k = E as special cases; bucketing against a
 dictionary-based brute force."""
 
+import math
+
 import mpmath
 import numpy as np
 import pytest
@@ -93,6 +95,54 @@ def test_k_equals_e_selects_all_in_order():
     for t in range(5):
         assert sorted(ids[t]) == list(range(16))
         assert np.all(np.diff(logits[t, ids[t]]) <= 0)
+
+
+@pytest.mark.parametrize("k", [1, 4, 8])
+def test_topk_sel_against_sort_and_mpmath(k):
+    """Selection-only bias: picks = stable sort of -(logits + bias), weights =
+    mpmath sigmoid of the unbiased logits, renormalised over the picks."""
+    x, wr, b = _routing_inputs(bias=True)
+    logits = oracle.router_logits(x, wr)
+    for renorm in (0, 1):
+        ids, w = oracle.topk_sel(logits, b, k, renorm)
+        key = logits + b.astype(np.float64)
+        assert np.array_equal(ids, np.argsort(-key, axis=1, kind="stable")[:, :k])
+        mpmath.mp.dps = 40
+        for t in range(logits.shape[0]):
+            s = [1 / (1 + mpmath.exp(-mpmath.mpf(float(logits[t, e])))) for e in ids[t]]
+            tot = sum(s) if renorm else 1
+            assert np.array_equal(w[t], np.array([float(si / tot) for si in s], np.float32))
+
+
+def test_topk_sel_hand_example():
+    """logits (1, 2, 3, 0), bias (5, 0, 0, 0), k = 2: the bias lifts expert 0
+    to the top (score 6), expert 2 (score 3) is second; the weights are
+    sigmoid(1) and sigmoid(3) over their sum, not sigmoid(6) and sigmoid(3)."""
+    logits = np.array([[1.0, 2.0, 3.0, 0.0]])
+    bias = np.array([5.0, 0.0, 0.0, 0.0], np.float32)
+    ids, w = oracle.topk_sel(logits, bias, 2)
+    assert ids.tolist() == [[0, 2]]
+    s1, s3 = 1 / (1 + math.exp(-1.0)), 1 / (1 + math.exp(-3.0))
+    assert np.array_equal(w[0], np.array([s1 / (s1 + s3), s3 / (s1 + s3)], np.float32))
+    ids_b, w_b = oracle.topk(logits + bias, 2)  # bias in the logit: same picks
+    assert ids_b.tolist() == [[0, 2]] and not np.array_equal(w_b, w)
+
+
+def test_topk_sel_zero_bias_is_topk():
+    x, wr, _ = _routing_inputs()
+    logits = oracle.router_logits(x, wr)
+    ids, w = oracle.topk_sel(logits, np.zeros(logits.shape[1], np.float32), 8)
+    ids0, w0 = oracle.topk(logits, 8)
+    assert np.array_equal(ids, ids0) and np.array_equal(w, w0)
+
+
+def test_forward_bias_mode_1_writes_unbiased_logits():
+    cfg = get_config("tiny").with_(E=16, n_local=8, topk=4, bias_kind="local", beta=0.3, bias_mode=1)
+    inp = make_inputs(cfg, 2)
+    got = oracle.forward(inp)
+    assert np.array_equal(got["logits"], oracle.router_logits(inp["x"], inp["wr"]))
+    ids, w = oracle.topk_sel(got["logits"], inp["bias"], cfg.topk)
+    assert np.array_equal(got["ids"], ids) and np.array_equal(got["w"], w)
 
 
 def _brute_bucket(ids, n_loc, base):
