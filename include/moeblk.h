@@ -233,6 +233,80 @@ int moe_forward(const moe_dims* dims, const void* x, const float* w_router, cons
                 int32_t* pick_pos, int32_t* active, void* y, float* out, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* around the block: the latent projections                                  */
+/* ------------------------------------------------------------------------ */
+
+/* The steps next to the block (Muse Spark K5 page, HA routing tail and HB;
+ * K3 page, stages "A" and "F"; the Kimi-K3 layer page's latent MoE in
+ * "k2_launch": w_ld, ln_w, w_up):
+ *   before: ffn_in [S, D] feeds the router and pre_expert_proj, a dense bf16
+ *           projection to the latent width L the experts run on (a GPU holds
+ *           a share of its rows); after the gather, pre_expert_norm gives the
+ *           experts' input h [S, L];
+ *   after:  post_expert_proj maps the summed expert partial [S, L] back to
+ *           the model width (a share of its rows a GPU).
+ * Sizes (elements). Supported ranges: 1 <= S <= 128; 128 <= K <= 16384,
+ * K % 128 == 0; 64 <= N <= 16384, N % 64 == 0; 0 <= E <= 256; bias_mode in
+ * {0, 1}; eps finite, >= 0. */
+typedef struct moe_proj_dims {
+  int32_t S;         /* token rows */
+  int32_t K;         /* input width: D (moe_pre_expert) or L (moe_post_expert) */
+  int32_t N;         /* weight rows held here = outputs a token (moe_latent_norm: L) */
+  int32_t E;         /* moe_pre_expert: router rows held here, 0 = no router */
+  int32_t bias_mode; /* moe_pre_expert: as moe_dims.bias_mode */
+  float eps;         /* moe_latent_norm: RMSNorm epsilon */
+} moe_proj_dims;
+
+/* Host-only check of `dims`: MOE_OK, MOE_ERR_NULL, _SHAPE or _UNSUPPORTED. */
+int moe_check_proj_dims(const moe_proj_dims* dims);
+
+/* Packed size (N * K * 2 bytes, 0 if `dims` is invalid) and packing of a
+ * dense bf16 weight w [N, K] (row n = output n) into the kernels' tile order.
+ * The packed buffer is opaque: only moe_pre_expert / moe_post_expert read it. */
+size_t moe_packed_dense_bytes(const moe_proj_dims* dims);
+int moe_pack_dense(const moe_proj_dims* dims, const void* w, void* packed, hipStream_t stream);
+
+/* Workspace bytes of moe_pre_expert / moe_post_expert (fp32 split-K
+ * partials and a bf16 copy of the post input); 0 if `dims` is invalid. No
+ * initial contents are needed; calls sharing one workspace must not overlap. */
+size_t moe_proj_workspace_bytes(const moe_proj_dims* dims);
+
+/* Before the block (K5 page, HA: router and pre_expert_proj on ffn_in):
+ *   ffn_in   [S, K] bf16;
+ *   w_packed moe_pack_dense of w_pre [N, K] bf16;
+ *   w_router [E, K] fp32, bias [E] fp32 or NULL, logits [S, E] fp32: as
+ *            moe_route's logits (ignored when E == 0, may be NULL then);
+ *   h_raw    [S, N] bf16, written: bf16(sum_k ffn_in[t][k] w_pre[n][k]),
+ *            fp32 accumulation in K parts summed in part order, one rounding.
+ * Router and projection are two launches, then one to finish the parts. */
+int moe_pre_expert(const moe_proj_dims* dims, const void* ffn_in, const void* w_packed,
+                   const float* w_router, const float* bias, float* logits, void* h_raw,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* pre_expert_norm (K5 page, HA: one token a CTA), on the whole latent:
+ *   h_raw [S, N] bf16 (N = L), gamma [N] bf16 or NULL (ones);
+ *   h     [S, N] bf16, written: bf16(h_raw * r * gamma) with
+ *         r = (sum_c h_raw[t][c]^2 / N + eps)^(-1/2), evaluated in fp64. */
+int moe_latent_norm(const moe_proj_dims* dims, const void* h_raw, const void* gamma, void* h,
+                    hipStream_t stream);
+
+/* After the block (K3 page, stage "F"; K5 page, HB: post_expert_proj of the
+ * summed expert partial):
+ *   partial  [S, K] fp32 (the partials of all GPUs summed), rounded to bf16
+ *            for the bf16 GEMM;
+ *   w_packed moe_pack_dense of w_post [N, K] bf16;
+ *   out      [S, N] bf16, written: bf16(sum_k bf16(partial[t][k]) w_post[n][k]),
+ *            fp32 accumulation as in moe_pre_expert. */
+int moe_post_expert(const moe_proj_dims* dims, const float* partial, const void* w_packed,
+                    void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Top-k of given logits (the router part of moe_route alone), for logits
+ * that moe_pre_expert computed: the arguments are moe_route's. With
+ * bias_mode 0 the logits already hold the bias and `bias` is not read. */
+int moe_topk(const moe_dims* dims, const float* logits, const float* bias, int32_t* topk_ids,
+             float* topk_w, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

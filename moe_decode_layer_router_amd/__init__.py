@@ -33,6 +33,16 @@ __all__ = [
     "moe_combine",
     "moe_forward_workspace_bytes",
     "moe_forward",
+    "MoeProjDims",
+    "proj_dims_from",
+    "moe_check_proj_dims",
+    "moe_packed_dense_bytes",
+    "moe_pack_dense",
+    "moe_proj_workspace_bytes",
+    "moe_pre_expert",
+    "moe_latent_norm",
+    "moe_post_expert",
+    "moe_topk",
     "MOE_W13",
     "MOE_W2",
 ]
@@ -70,6 +80,17 @@ class MoeDims(ctypes.Structure):
     @property
     def r_max(self) -> int:
         return self.S * min(self.topk, self.n_local)
+
+
+class MoeProjDims(ctypes.Structure):
+    _fields_ = [
+        ("S", ctypes.c_int32),
+        ("K", ctypes.c_int32),
+        ("N", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("bias_mode", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
 
 
 class MoeError(RuntimeError):
@@ -117,9 +138,20 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_workspace_bytes.argtypes = [_DP]
         L.moe_forward_workspace_bytes.restype = ctypes.c_size_t
         L.moe_forward.argtypes = [_DP] + [_P] * 19 + [ctypes.c_size_t, _P]
+        _PD = ctypes.POINTER(MoeProjDims)
+        L.moe_check_proj_dims.argtypes = [_PD]
+        for f in ("moe_packed_dense_bytes", "moe_proj_workspace_bytes"):
+            getattr(L, f).argtypes = [_PD]
+            getattr(L, f).restype = ctypes.c_size_t
+        L.moe_pack_dense.argtypes = [_PD, _P, _P, _P]
+        L.moe_pre_expert.argtypes = [_PD] + [_P] * 7 + [ctypes.c_size_t, _P]
+        L.moe_latent_norm.argtypes = [_PD, _P, _P, _P, _P]
+        L.moe_post_expert.argtypes = [_PD] + [_P] * 4 + [ctypes.c_size_t, _P]
+        L.moe_topk.argtypes = [_DP, _P, _P, _P, _P, _P]
         for f in (
             "moe_pack_mxfp4", "moe_pack_bf16", "moe_route", "moe_bucket", "moe_expert_ffn", "moe_combine",
-            "moe_forward",
+            "moe_forward", "moe_check_proj_dims", "moe_pack_dense", "moe_pre_expert", "moe_latent_norm",
+            "moe_post_expert", "moe_topk",
         ):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -250,4 +282,65 @@ def moe_forward(dims, x, w_router, bias, w13_packed, w2_packed, ws13_packed, ws2
         _ptr(w2_packed), _ptr(ws13_packed), _ptr(ws2_packed), _ptr(gamma), _ptr(logits), _ptr(topk_ids),
         _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(rows), _ptr(pick_pos), _ptr(active), _ptr(y), _ptr(out),
         _ptr(workspace), int(workspace_bytes), _stream(stream),
+    )
+
+
+# ---------------------------------------------------------------- around the block
+
+
+def proj_dims_from(cfg) -> MoeProjDims:
+    """MoeProjDims from an object or dict with the moe_proj_dims field names."""
+    get = cfg.get if isinstance(cfg, dict) else (lambda k, dflt=None: getattr(cfg, k, dflt))
+    return MoeProjDims(
+        S=get("S"), K=get("K"), N=get("N"), E=get("E", 0), bias_mode=get("bias_mode", 0), eps=get("eps", 1e-6),
+    )
+
+
+def _pd(dims) -> MoeProjDims:
+    return dims if isinstance(dims, MoeProjDims) else proj_dims_from(dims)
+
+
+def moe_check_proj_dims(dims) -> int:
+    return lib().moe_check_proj_dims(ctypes.byref(_pd(dims)))
+
+
+def moe_packed_dense_bytes(dims) -> int:
+    return lib().moe_packed_dense_bytes(ctypes.byref(_pd(dims)))
+
+
+def moe_pack_dense(dims, w, packed, stream=None) -> None:
+    _call("moe_pack_dense", ctypes.byref(_pd(dims)), _ptr(w), _ptr(packed), _stream(stream))
+
+
+def moe_proj_workspace_bytes(dims) -> int:
+    return lib().moe_proj_workspace_bytes(ctypes.byref(_pd(dims)))
+
+
+def moe_pre_expert(dims, ffn_in, w_packed, w_router, bias, logits, h_raw, workspace, workspace_bytes=None,
+                   stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _call(
+        "moe_pre_expert", ctypes.byref(_pd(dims)), _ptr(ffn_in), _ptr(w_packed), _ptr(w_router), _ptr(bias),
+        _ptr(logits), _ptr(h_raw), _ptr(workspace), int(workspace_bytes), _stream(stream),
+    )
+
+
+def moe_latent_norm(dims, h_raw, gamma, h, stream=None) -> None:
+    _call("moe_latent_norm", ctypes.byref(_pd(dims)), _ptr(h_raw), _ptr(gamma), _ptr(h), _stream(stream))
+
+
+def moe_post_expert(dims, partial, w_packed, out, workspace, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _call(
+        "moe_post_expert", ctypes.byref(_pd(dims)), _ptr(partial), _ptr(w_packed), _ptr(out), _ptr(workspace),
+        int(workspace_bytes), _stream(stream),
+    )
+
+
+def moe_topk(dims, logits, bias, topk_ids, topk_w, stream=None) -> None:
+    _call(
+        "moe_topk", ctypes.byref(_d(dims)), _ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(topk_w),
+        _stream(stream),
     )

@@ -151,3 +151,53 @@ class MoeBlock:
     def forward_error(self) -> int:
         """moe_forward's wait-bound error word (0: no wait hit its bound)."""
         return self._error_word(self.fws)
+
+
+class ProjSteps:
+    """Device buffers of the steps around the block for inputs from
+    ``synth.make_proj_inputs``: the pre-expert step (router + pre projection
+    of this GPU's rows), the latent norm (on a gathered [S, L] projection) and
+    the post-expert step (this GPU's rows). Allocates only here."""
+
+    def __init__(self, inp: dict, device="cuda"):
+        from . import moe_pack_dense, moe_packed_dense_bytes, moe_proj_workspace_bytes, proj_dims_from
+
+        pc = inp["cfg"]
+        self.pc = pc
+        dv = torch.device(device)
+        S, D, L = pc.S, pc.D, pc.L
+        self.pre_dims = proj_dims_from(dict(S=S, K=D, N=pc.n_pre, E=pc.e_router, bias_mode=pc.bias_mode))
+        self.norm_dims = proj_dims_from(dict(S=S, K=L, N=L, eps=pc.eps))
+        self.post_dims = proj_dims_from(dict(S=S, K=L, N=pc.n_post))
+        self.ffn_in = bf16_tensor(inp["ffn_in"], dv)
+        self.wr = _dev(inp["wr_pre"], dv) if pc.e_router else None
+        self.bias = _dev(inp.get("bias_pre"), dv)
+        self.w_pre = torch.empty(moe_packed_dense_bytes(self.pre_dims), dtype=torch.uint8, device=dv)
+        moe_pack_dense(self.pre_dims, bf16_tensor(inp["w_pre"], dv), self.w_pre)
+        self.logits = torch.empty((S, max(pc.e_router, 1)), dtype=torch.float32, device=dv)
+        self.h_raw = torch.empty((S, pc.n_pre), dtype=torch.bfloat16, device=dv)
+        self.ws_pre = torch.empty(moe_proj_workspace_bytes(self.pre_dims), dtype=torch.uint8, device=dv)
+        self.norm_in = bf16_tensor(inp["h_raw"], dv)
+        self.gamma = bf16_tensor(inp.get("gamma_l"), dv)
+        self.h = torch.empty((S, L), dtype=torch.bfloat16, device=dv)
+        self.partial = _dev(inp["partial"], dv)
+        self.w_post = torch.empty(moe_packed_dense_bytes(self.post_dims), dtype=torch.uint8, device=dv)
+        moe_pack_dense(self.post_dims, bf16_tensor(inp["w_post"], dv), self.w_post)
+        self.out = torch.empty((S, pc.n_post), dtype=torch.bfloat16, device=dv)
+        self.ws_post = torch.empty(moe_proj_workspace_bytes(self.post_dims), dtype=torch.uint8, device=dv)
+
+    def pre(self):
+        from . import moe_pre_expert
+
+        moe_pre_expert(self.pre_dims, self.ffn_in, self.w_pre, self.wr, self.bias,
+                       self.logits if self.pc.e_router else None, self.h_raw, self.ws_pre)
+
+    def norm(self):
+        from . import moe_latent_norm
+
+        moe_latent_norm(self.norm_dims, self.norm_in, self.gamma, self.h)
+
+    def post(self):
+        from . import moe_post_expert
+
+        moe_post_expert(self.post_dims, self.partial, self.w_post, self.out, self.ws_post)

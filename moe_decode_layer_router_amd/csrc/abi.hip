@@ -1,4 +1,4 @@
-// abi.hip -- version, status strings and the dims check (host only).
+// abi.hip -- version, status strings and the dims checks (host only).
 #include <math.h>
 
 #include "host.h"
@@ -18,6 +18,17 @@ int check_dims(const moe_dims* d) {
                   (d->shared_I >= 128 && d->shared_I <= 8192 && d->shared_I % 128 == 0),
               MOE_ERR_SHAPE);
   MOE_REQUIRE(d->renorm == 0 || d->renorm == 1, MOE_ERR_UNSUPPORTED);
+  MOE_REQUIRE(d->bias_mode == 0 || d->bias_mode == 1, MOE_ERR_UNSUPPORTED);
+  MOE_REQUIRE(isfinite(d->eps) && d->eps >= 0.0f, MOE_ERR_UNSUPPORTED);
+  return MOE_OK;
+}
+
+int check_proj_dims(const moe_proj_dims* d) {
+  MOE_REQUIRE(d != nullptr, MOE_ERR_NULL);
+  MOE_REQUIRE(d->S >= 1 && d->S <= 128, MOE_ERR_SHAPE);
+  MOE_REQUIRE(d->K >= 128 && d->K <= 16384 && d->K % 128 == 0, MOE_ERR_SHAPE);
+  MOE_REQUIRE(d->N >= 64 && d->N <= 16384 && d->N % 64 == 0, MOE_ERR_SHAPE);
+  MOE_REQUIRE(d->E >= 0 && d->E <= 256, MOE_ERR_SHAPE);
   MOE_REQUIRE(d->bias_mode == 0 || d->bias_mode == 1, MOE_ERR_UNSUPPORTED);
   MOE_REQUIRE(isfinite(d->eps) && d->eps >= 0.0f, MOE_ERR_UNSUPPORTED);
   return MOE_OK;

@@ -119,22 +119,6 @@ ffn_single_kernel(FfnArgs a) {
                                        WaitFlag{&a.ready[t * kCtlStride], a.error}, red);
 }
 
-// Shared expert task t of n_sg token groups x RB row blocks -> (row block,
-// group). Workgroups go to the 8 XCDs round-robin by id, so the groups of one
-// row block get ids that are equal mod 8 and adjacent in that XCD's order:
-// they run together on one XCD and share its L2 for the row block's weights.
-__device__ __forceinline__ void shared_task(int t, int n_sg, int RB, int& rb, int& grp) {
-  constexpr int kXcd = 8;
-  if (RB % kXcd == 0) {
-    const int slot = t / kXcd;
-    grp = slot % n_sg;
-    rb = (slot / n_sg) * kXcd + t % kXcd;
-  } else {
-    rb = t / n_sg;
-    grp = t - rb * n_sg;
-  }
-}
-
 template <int TTG, int P, bool kShared>
 __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
   __shared__ f32x4_t red[kSplit][kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave];
@@ -146,7 +130,7 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
     const int n_sg = (a.S + GS - 1) / GS;
     if (t < n_sg * RBs) {
       int rb, grp;
-      shared_task(t, n_sg, RBs, rb, grp);
+      group_task(t, n_sg, RBs, rb, grp);
       const int row0 = grp * GS, ntok = min(GS, a.S - row0);
       const uint8_t* tiles = a.ws13 + static_cast<size_t>(rb) * NC * kBfTileBytes;
       ffn_task<false, kSharedTTG, kSharedP, true, false>(
@@ -181,7 +165,7 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
     if (t < n_sg * RB) {
       const int NCs = a.Is / kChunkK;
       int rb, grp;
-      shared_task(t, n_sg, RB, rb, grp);
+      group_task(t, n_sg, RB, rb, grp);
       const int row0 = grp * GS, ntok = min(GS, a.S - row0);
       const uint8_t* tiles = a.ws2 + static_cast<size_t>(rb) * NCs * kBfTileBytes;
       ffn_task<false, kSharedTTG, kSharedP, false, false>(

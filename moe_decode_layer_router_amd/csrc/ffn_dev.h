@@ -71,6 +71,23 @@ __device__ __forceinline__ int count_work(int cnt) {
   return ng;
 }
 
+// Dense weights read by several token groups: task t of n_g token groups x
+// RB weight blocks -> (block, group). Workgroups go to the 8 XCDs round-robin
+// by id, so the groups of one block get ids that are equal mod 8 and adjacent
+// in that XCD's order: they run together on one XCD and share its L2 for the
+// block's weights.
+__device__ __forceinline__ void group_task(int t, int n_g, int RB, int& rb, int& grp) {
+  constexpr int kXcd = 8;
+  if (RB % kXcd == 0) {
+    const int slot = t / kXcd;
+    grp = slot % n_g;
+    rb = (slot / n_g) * kXcd + t % kXcd;
+  } else {
+    rb = t / n_g;
+    grp = t - rb * n_g;
+  }
+}
+
 template <int TTG>
 struct MxChunk {
   u32x4_t w[4];       // 4 row tiles x 32 e2m1 codes a lane
@@ -133,9 +150,9 @@ __device__ __forceinline__ void load_w(MxChunk<TTG>& ch, const uint8_t* wlane, c
   ch.s = ld_nt<uint32_t>(slane + static_cast<size_t>(c) * kMxTileBytes);
 }
 
-// The shared expert's tiles are read once per token group, by tasks placed on
-// one XCD (see the shared task order in ffn.hip): plain loads, so the groups
-// after the first find them in that XCD's L2.
+// Dense bf16 tiles (the shared expert, the latent projections) are read once
+// per token group, by tasks placed on one XCD (group_task): plain loads, so
+// the groups after the first find them in that XCD's L2.
 template <int TTG>
 __device__ __forceinline__ void load_w(BfChunk<TTG>& ch, const uint8_t* wlane, const uint8_t*,
                                        int c) {
@@ -189,8 +206,10 @@ struct NoWait {
 // bucket row (row length out_ld); before_b() runs after the weight prefetch and
 // before the first activation load; red: LDS. kCoh: the SwiGLU rows pass
 // between workgroups of one launch (gate_up writes them through to the
-// coherence point, down reads them from there).
-template <bool kMx, int TTG, int P, bool kGateUp, bool kCoh, class SrcOf, class BeforeB>
+// coherence point, down reads them from there). kF32Out (not gate_up): out
+// holds fp32 rows (a split-K partial), written unrounded.
+template <bool kMx, int TTG, int P, bool kGateUp, bool kCoh, bool kF32Out = false, class SrcOf,
+          class BeforeB>
 __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int NC,
                                          const uint16_t* __restrict__ bsrc, int K, int row0,
                                          int ntok, int rb, uint16_t* __restrict__ out, int out_ld,
@@ -282,6 +301,10 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
       uint32_t* hp = reinterpret_cast<uint32_t*>(orow + i0);
       if constexpr (kCoh) __hip_atomic_store(hp, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else *hp = hv;
+    } else if constexpr (kF32Out) {
+      const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
+      float* frow = reinterpret_cast<float*>(out) + static_cast<size_t>(row0 + c) * out_ld;
+      *reinterpret_cast<f32x4_t*>(frow + n0) = s;
     } else {
       const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
       *reinterpret_cast<u32x2_t*>(orow + n0) =

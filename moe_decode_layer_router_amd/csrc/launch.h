@@ -22,6 +22,8 @@ void launch_topk(const moe_dims& m, const float* logits, const float* bias, int3
                  hipStream_t stream);
 void launch_bucket(const moe_dims& m, const int32_t* ids, int32_t* counts, int32_t* offsets,
                    int32_t* rows, int32_t* pick_pos, int32_t* active, hipStream_t stream);
+// dense bf16 [N][K] -> the bf16 tile order (the down-projection row order)
+void launch_pack_bf16(const uint16_t* w, void* packed, int N, int K, hipStream_t stream);
 void launch_combine(const moe_dims& m, const void* y, const float* w, const int32_t* pick_pos,
                     const void* gamma, float* out, hipStream_t stream);
 

@@ -61,6 +61,13 @@ bool weight_shape(const moe_dims& m, int which, bool shared, int& N, int& K) {
 }
 
 }  // namespace
+
+void launch_pack_bf16(const uint16_t* w, void* packed, int N, int K, hipStream_t stream) {
+  const int RB = N / kRowsPerBlock, NC = K / kChunkK;
+  hipLaunchKernelGGL(pack_bf16_kernel, dim3(RB * NC), dim3(256), 0, stream, w,
+                     static_cast<uint8_t*>(packed), static_cast<int>(MOE_W2), N, K, NC);
+}
+
 }  // namespace moeblk
 
 using namespace moeblk;
@@ -101,9 +108,13 @@ extern "C" int moe_pack_bf16(const moe_dims* dims, int which, const void* w, voi
   MOE_REQUIRE(weight_shape(*dims, which, true, N, K), MOE_ERR_UNSUPPORTED);
   MOE_REQUIRE(w && packed, MOE_ERR_NULL);
   MOE_REQUIRE(aligned16(w) && aligned16(packed), MOE_ERR_ALIGN);
-  const int RB = N / kRowsPerBlock, NC = K / kChunkK;
-  hipLaunchKernelGGL(pack_bf16_kernel, dim3(RB * NC), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(w), static_cast<uint8_t*>(packed), which, N, K,
-                     NC);
+  if (which == MOE_W2) {
+    launch_pack_bf16(static_cast<const uint16_t*>(w), packed, N, K, stream);
+  } else {
+    const int RB = N / kRowsPerBlock, NC = K / kChunkK;
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(RB * NC), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(w), static_cast<uint8_t*>(packed), which, N, K,
+                       NC);
+  }
   return launch_status();
 }

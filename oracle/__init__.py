@@ -61,6 +61,9 @@ def _declare(L):
     L.orc_norm_row.argtypes = [_I, _P, _P, _D, _P]
     L.orc_combine.argtypes = [_I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P]
     L.orc_topk_sel.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
+    L.orc_dense_proj.argtypes = [_I, _I, _I, _P, _P, _P]
+    L.orc_latent_norm.argtypes = [_I, _I, ctypes.c_double, _P, _P, _P]
+    L.orc_post_proj.argtypes = [_I, _I, _I, _P, _P, _P]
     L.orc_forward.argtypes = [_I] * 8 + [_F, _I, _I] + [_P] * 20
     for f in (
         "orc_router_logits",
@@ -77,6 +80,9 @@ def _declare(L):
         "orc_expert_ffn",
         "orc_norm_row",
         "orc_combine",
+        "orc_dense_proj",
+        "orc_latent_norm",
+        "orc_post_proj",
         "orc_forward",
     ):
         getattr(L, f).restype = _I
@@ -343,3 +349,37 @@ def forward(inp: dict) -> dict:
         logits=logits, ids=ids, w=w, counts=counts, offsets=offsets, rows=rows[:R_max],
         pick_pos=pick_pos, active=active, y=y, out=out,
     )
+
+
+# ---------------------------------------------------------------- around the block
+
+
+def dense_proj(inp, w) -> np.ndarray:
+    """bf16 bits [S][K] x bf16 bits [N][K] -> bf16 bits [S][N] (fp64 sums)."""
+    inp = _c(inp, np.uint16)
+    w = _c(w, np.uint16)
+    S, K = inp.shape
+    N = w.shape[0]
+    out = np.empty((S, N), np.uint16)
+    _chk(lib().orc_dense_proj(S, K, N, _ptr(inp), _ptr(w), _ptr(out)), "dense_proj")
+    return out
+
+
+def latent_norm(h_raw, gamma=None, eps=1e-6) -> np.ndarray:
+    h_raw = _c(h_raw, np.uint16)
+    gamma = _c(gamma, np.uint16)
+    S, L = h_raw.shape
+    out = np.empty((S, L), np.uint16)
+    _chk(lib().orc_latent_norm(S, L, float(eps), _ptr(h_raw), _ptr(gamma), _ptr(out)), "latent_norm")
+    return out
+
+
+def post_proj(partial, w) -> np.ndarray:
+    """fp32 [S][K] (rounded to bf16 first) x bf16 bits [N][K] -> bf16 bits [S][N]."""
+    partial = _c(partial, np.float32)
+    w = _c(w, np.uint16)
+    S, K = partial.shape
+    N = w.shape[0]
+    out = np.empty((S, N), np.uint16)
+    _chk(lib().orc_post_proj(S, K, N, _ptr(partial), _ptr(w), _ptr(out)), "post_proj")
+    return out

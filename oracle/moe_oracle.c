@@ -16,7 +16,10 @@
  *      (K3 page, stages "C, D": MXFP4 weights decoded, bf16 MFMA);
  *   4. per-pick RMSNorm of the expert output
  *      (K3 page, stage "E"; the RMSNorm form of the KDA page, "kda_norm");
- *   5. the routing-weighted sum into an fp32 partial (K3 page, stage "E").
+ *   5. the routing-weighted sum into an fp32 partial (K3 page, stage "E");
+ *   6. around the block: the dense latent projection before it and its norm,
+ *      and the projection of the summed partial after it (K5 page, HA and
+ *      HB; K3 page, stages "A" and "F").
  *
  * Precision: every sum is an fp64 sum in index order; the products of bf16 or
  * fp32 inputs with decoded MXFP4 weights are exact in fp64. The KDA page's
@@ -430,6 +433,62 @@ int orc_combine(int S, int d, int topk, int n_loc, int Is, float eps, const uint
   free(acc);
   free(z);
   return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 6. the latent projections around the block                                */
+/* ------------------------------------------------------------------------ */
+
+/* K5 page, HA routing tail: ffn_in feeds both the router and pre_expert_proj,
+ * a dense bf16 projection into the latent the experts run on, and the
+ * projection is normalised (pre_expert_norm) before the experts. K3 page,
+ * stage "F", and K5 page, HB: post_expert_proj maps the summed expert partial
+ * back. (The Kimi-K3 layer page's latent MoE has the same chain: "k2_launch"
+ * takes w_ld, ln_w and w_up.) */
+
+/* out[t][n] = bf16( sum_k in[t][k] * w[n][k] ), in [S][K] and w [N][K] bf16 */
+int orc_dense_proj(int S, int K, int N, const uint16_t* in, const uint16_t* w, uint16_t* out) {
+  if (S < 0 || K <= 0 || N <= 0 || !in || !w || !out) return ORC_EINVAL;
+  for (int t = 0; t < S; ++t)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k)
+        acc += orc_bf16_to_f64(in[(long)t * K + k]) * orc_bf16_to_f64(w[(long)n * K + k]);
+      out[(long)t * N + n] = orc_f64_to_bf16(acc);
+    }
+  return ORC_OK;
+}
+
+/* pre_expert_norm: h[t][c] = bf16( h_raw[t][c] * r_t * gamma[c] ) with
+ * r_t = (sum_c h_raw[t][c]^2 / L + eps)^(-1/2); gamma NULL = ones */
+int orc_latent_norm(int S, int L, double eps, const uint16_t* h_raw, const uint16_t* gamma,
+                    uint16_t* h) {
+  if (S < 0 || L <= 0 || !h_raw || !h) return ORC_EINVAL;
+  for (int t = 0; t < S; ++t) {
+    double ss = 0.0;
+    for (int c = 0; c < L; ++c) {
+      double v = orc_bf16_to_f64(h_raw[(long)t * L + c]);
+      ss += v * v;
+    }
+    double r = 1.0 / sqrt(ss / (double)L + eps);
+    for (int c = 0; c < L; ++c) {
+      double g = gamma ? orc_bf16_to_f64(gamma[c]) : 1.0;
+      h[(long)t * L + c] = orc_f64_to_bf16(orc_bf16_to_f64(h_raw[(long)t * L + c]) * r * g);
+    }
+  }
+  return ORC_OK;
+}
+
+/* post_expert_proj: the fp32 partial is handed to the bf16 GEMM rounded to
+ * bf16, then out = orc_dense_proj of it */
+int orc_post_proj(int S, int K, int N, const float* partial, const uint16_t* w, uint16_t* out) {
+  if (S < 0 || K <= 0 || N <= 0 || !partial || !w || !out) return ORC_EINVAL;
+  uint16_t* in = (uint16_t*)malloc(sizeof(uint16_t) * ((size_t)S * K + 1));
+  if (!in) return ORC_EINVAL;
+  for (long i = 0; i < (long)S * K; ++i) in[i] = orc_f64_to_bf16((double)partial[i]);
+  int rc = orc_dense_proj(S, K, N, in, w, out);
+  free(in);
+  return rc;
 }
 
 /* ------------------------------------------------------------------------ */

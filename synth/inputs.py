@@ -28,7 +28,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import MoeConfig
+from .configs import MoeConfig, ProjConfig
 
 # stream ids: fixed forever so stored seeds keep their meaning
 _STREAM = {
@@ -41,6 +41,13 @@ _STREAM = {
     "gamma": 7,
     "ws13": 8,
     "ws2": 9,
+    "ffn_in": 10,
+    "w_pre": 11,
+    "wr_pre": 12,
+    "gamma_l": 13,
+    "h_raw": 14,
+    "partial": 15,
+    "w_post": 16,
 }
 
 
@@ -154,4 +161,39 @@ def make_inputs(
             if Is
             else None
         )
+    return out
+
+
+def make_proj_inputs(pc: ProjConfig, seed: int = 0, *, gamma: str = "random") -> dict:
+    """Inputs of the steps around the block:
+
+    =========  =====================  ==============================
+    ffn_in     [S, D]                 bf16 bits, N(0, x_std)
+    w_pre      [n_pre, D]             bf16 bits, N(0, w_std)
+    wr_pre     [e_router, D]          float32, N(0, wr_std)
+    gamma_l    [L] or None            bf16 bits, 1 + 0.1 N(0, 1)
+    h_raw      [S, L]                 bf16 bits, N(0, w_std sqrt(D)): a
+                                      gathered projection for the norm
+    partial    [S, L]                 float32, N(0, partial_std)
+    w_post     [n_post, L]            bf16 bits, N(0, w_std)
+    =========  =====================  =============================="""
+    S, D, L = pc.S, pc.D, pc.L
+    out: dict = {"cfg": pc, "seed": seed}
+    out["ffn_in"] = f32_to_bf16_bits(_rng(seed, "ffn_in").standard_normal((S, D), dtype=np.float32) * pc.x_std)
+    out["w_pre"] = f32_to_bf16_bits(_rng(seed, "w_pre").standard_normal((pc.n_pre, D), dtype=np.float32) * pc.w_std)
+    out["wr_pre"] = (
+        _rng(seed, "wr_pre").standard_normal((pc.e_router, D), dtype=np.float32) * pc.wr_std
+    ).astype(np.float32)
+    if gamma == "ones":
+        out["gamma_l"] = None
+    else:
+        out["gamma_l"] = f32_to_bf16_bits(1.0 + 0.1 * _rng(seed, "gamma_l").standard_normal(L, dtype=np.float32))
+    std_h = pc.w_std * float(np.sqrt(D))
+    out["h_raw"] = f32_to_bf16_bits(_rng(seed, "h_raw").standard_normal((S, L), dtype=np.float32) * std_h)
+    out["partial"] = (
+        _rng(seed, "partial").standard_normal((S, L), dtype=np.float32) * pc.partial_std
+    ).astype(np.float32)
+    out["w_post"] = f32_to_bf16_bits(
+        _rng(seed, "w_post").standard_normal((pc.n_post, L), dtype=np.float32) * pc.w_std
+    )
     return out

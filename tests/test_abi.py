@@ -181,3 +181,88 @@ def test_python_binding_refuses_cpu_tensors():
 
     with pytest.raises(ValueError):
         mb.moe_combine(dims(), torch.zeros(4), torch.zeros(4), torch.zeros(4), None, torch.zeros(4))
+
+
+# ------------------------------------------------------------ around the block
+
+
+def pdims(**kw):
+    base = dict(S=8, K=8192, N=512, E=32, bias_mode=0, eps=1e-6)
+    base.update(kw)
+    return mb.proj_dims_from(base)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(), mb.MOE_OK),
+        (dict(E=0), mb.MOE_OK),
+        (dict(S=128, K=16384, N=16384, E=256), mb.MOE_OK),
+        (dict(S=1, K=128, N=64), mb.MOE_OK),
+        (dict(S=0), mb.MOE_ERR_SHAPE),
+        (dict(S=129), mb.MOE_ERR_SHAPE),
+        (dict(K=100), mb.MOE_ERR_SHAPE),
+        (dict(K=16512), mb.MOE_ERR_SHAPE),
+        (dict(N=32), mb.MOE_ERR_SHAPE),
+        (dict(N=96), mb.MOE_ERR_SHAPE),
+        (dict(E=-1), mb.MOE_ERR_SHAPE),
+        (dict(E=257), mb.MOE_ERR_SHAPE),
+        (dict(bias_mode=2), mb.MOE_ERR_UNSUPPORTED),
+        (dict(eps=-1.0), mb.MOE_ERR_UNSUPPORTED),
+        (dict(eps=float("inf")), mb.MOE_ERR_UNSUPPORTED),
+    ],
+)
+def test_check_proj_dims(kw, code):
+    assert mb.moe_check_proj_dims(pdims(**kw)) == code
+
+
+def test_proj_sizes():
+    d = pdims()
+    assert mb.moe_packed_dense_bytes(d) == 512 * 8192 * 2
+    assert mb.moe_packed_dense_bytes(pdims(N=10)) == 0
+    ws = mb.moe_proj_workspace_bytes(d)
+    assert ws >= 8 * 512 * 4 + 8 * 8192 * 2 and ws % 256 == 0
+    assert mb.moe_proj_workspace_bytes(pdims(S=0)) == 0
+
+
+def test_proj_calls_reject():
+    d = pdims()
+    pd = ctypes.byref(d)
+    need = mb.moe_proj_workspace_bytes(d)
+    # moe_pre_expert(dims, ffn_in, w, w_router, bias, logits, h_raw, ws, bytes, stream)
+    ok = [FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE]
+    pre = lambda dd, a, n=need: _rc("moe_pre_expert", dd, *a, n, None)  # noqa: E731
+    assert pre(None, ok) == mb.MOE_ERR_NULL
+    assert pre(ctypes.byref(pdims(K=100)), ok) == mb.MOE_ERR_SHAPE
+    for i in (0, 1, 2, 4, 5, 6):
+        a = list(ok)
+        a[i] = None
+        assert pre(pd, a) == mb.MOE_ERR_NULL, i
+        a[i] = MIS
+        assert pre(pd, a) == mb.MOE_ERR_ALIGN, i
+    a = list(ok)
+    a[2] = a[4] = None  # with router rows, their weights and logits are required
+    assert pre(pd, a) == mb.MOE_ERR_NULL
+    assert pre(pd, ok, need - 1) == mb.MOE_ERR_WORKSPACE
+    # moe_latent_norm(dims, h_raw, gamma, h, stream)
+    nd = ctypes.byref(pdims(N=4096))
+    assert _rc("moe_latent_norm", nd, None, None, FAKE, None) == mb.MOE_ERR_NULL
+    assert _rc("moe_latent_norm", nd, FAKE, MIS, FAKE, None) == mb.MOE_ERR_ALIGN
+    assert _rc("moe_latent_norm", ctypes.byref(pdims(eps=float("nan"))), FAKE, None, FAKE, None) == mb.MOE_ERR_UNSUPPORTED
+    # moe_post_expert(dims, partial, w, out, ws, bytes, stream)
+    post = lambda a, n=need: _rc("moe_post_expert", pd, *a, n, None)  # noqa: E731
+    for i in range(4):
+        a = [FAKE] * 4
+        a[i] = None
+        assert post(a) == mb.MOE_ERR_NULL, i
+        a[i] = MIS
+        assert post(a) == mb.MOE_ERR_ALIGN, i
+    assert post([FAKE] * 4, need - 1) == mb.MOE_ERR_WORKSPACE
+    # moe_pack_dense(dims, w, packed, stream)
+    assert _rc("moe_pack_dense", pd, None, FAKE, None) == mb.MOE_ERR_NULL
+    assert _rc("moe_pack_dense", pd, FAKE, MIS, None) == mb.MOE_ERR_ALIGN
+    # moe_topk(dims, logits, bias, ids, w, stream)
+    bd = ctypes.byref(dims())
+    assert _rc("moe_topk", bd, None, None, FAKE, FAKE, None) == mb.MOE_ERR_NULL
+    assert _rc("moe_topk", bd, FAKE, MIS, FAKE, FAKE, None) == mb.MOE_ERR_ALIGN
+    assert _rc("moe_topk", ctypes.byref(dims(S=0)), FAKE, None, FAKE, FAKE, None) == mb.MOE_ERR_SHAPE
