@@ -22,6 +22,8 @@ kernels run on, in a separate timed pass; its
 ``traffic`` comes from the committed rocprofv3 counter summary when that
 summary was taken on the current kernel sources, else null.
 ``cpu_baseline`` times the CPU oracle on the same workload.
+``around_block`` times the steps next to the block (moe_pre_expert,
+moe_latent_norm, moe_post_expert) at one GPU's share of their shapes.
 """
 
 from __future__ import annotations
@@ -95,6 +97,62 @@ def cpu_baseline(inp, budget_s: float) -> dict:
     }
 
 
+def around_block(S: int, warmup: int, K: int) -> dict:
+    """The steps next to the block at one rank's share of the K5 page's shapes
+    (d_model 8192, latent 4096): pre (32 router rows + 512 pre_expert_proj
+    rows on ffn_in), the latent norm on a gathered [S, 4096] projection, post
+    (1024 post_expert_proj rows). Weight copies rotate as for the block."""
+    import torch
+
+    from moe_decode_layer_router_amd.block import ProjSteps
+    from synth import PROJ_CONFIGS, make_proj_inputs
+
+    pc = PROJ_CONFIGS["latent_s8"].with_(S=S)
+    st = ProjSteps(make_proj_inputs(pc, 0), device="cuda:0")
+    b_w = pc.n_pre * pc.D * 2 + pc.e_router * pc.D * 4 + pc.n_post * pc.L * 2
+    n = max(1, math.ceil(2 * LLC_BYTES / b_w))
+    st.add_weight_copies(n - 1)
+    torch.cuda.synchronize()
+    res = {"workload": f"latent_s{S}: {pc.desc}", "weight_copies_rotated": n}
+    steps = {
+        "pre": (st.pre, pc.n_pre * pc.D * 2 + pc.e_router * pc.D * 4 + S * pc.D * 2 + S * pc.n_pre * 2
+                + S * pc.e_router * 4),
+        "norm": (st.norm, 2 * S * pc.L * 2 + pc.L * 2),
+        "post": (st.post, pc.n_post * pc.L * 2 + S * pc.L * 4 + S * pc.n_post * 2),
+    }
+    # These calls are a few microseconds of GPU work, less than the host needs
+    # to issue one, so they are timed as HIP graph replays: one graph holds
+    # one call per weight copy, replayed back to back between two events.
+    stream = torch.cuda.Stream()
+    for name, (fn, nbytes) in steps.items():
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i)
+        reps = max(1, K // n)
+        for _ in range(max(1, warmup // n)):
+            g.replay()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        med = t0.elapsed_time(t1) / (reps * n)
+        del g
+        gbps = nbytes / (med * 1e-3) / 1e9
+        res[name] = {"ms_per_call": round(med, 5), "algorithmic_bytes": nbytes, "gbps": round(gbps, 1),
+                     "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +164,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-around", action="store_true", help="skip the steps around the block")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -209,6 +268,8 @@ def main() -> int:
     read_gbps = big.numel() * 4 / (rd[len(rd) // 2] * 1e-3) / 1e9
     del big
 
+    around = None if args.no_around else around_block(cfg.S, args.warmup, K)
+
     tok_s = cfg.S / (ms * 1e-3)
     line = {
         "metric": "tokens/s and MXFP4 weight HBM GB/s (% of peak), local-expert MoE, S=8..128",
@@ -256,6 +317,7 @@ def main() -> int:
             "avg_ms": round(ffn_ms, 5),
         },
         "cpu_baseline": None,
+        "around_block": around,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

@@ -268,8 +268,10 @@ size_t moe_packed_dense_bytes(const moe_proj_dims* dims);
 int moe_pack_dense(const moe_proj_dims* dims, const void* w, void* packed, hipStream_t stream);
 
 /* Workspace bytes of moe_pre_expert / moe_post_expert (fp32 split-K
- * partials and a bf16 copy of the post input); 0 if `dims` is invalid. No
- * initial contents are needed; calls sharing one workspace must not overlap. */
+ * partials, counters, a bf16 copy of the post input); 0 if `dims` is
+ * invalid. The workspace must be zero-filled once before its first use; every
+ * call leaves its counters at zero again. Calls sharing one workspace must not
+ * overlap. */
 size_t moe_proj_workspace_bytes(const moe_proj_dims* dims);
 
 /* Before the block (K5 page, HA: router and pre_expert_proj on ffn_in):
@@ -279,7 +281,8 @@ size_t moe_proj_workspace_bytes(const moe_proj_dims* dims);
  *            moe_route's logits (ignored when E == 0, may be NULL then);
  *   h_raw    [S, N] bf16, written: bf16(sum_k ffn_in[t][k] w_pre[n][k]),
  *            fp32 accumulation in K parts summed in part order, one rounding.
- * Router and projection are two launches, then one to finish the parts. */
+ * One launch: the router rows are workgroups of the projection's launch (for
+ * K > 8192 the router has a launch of its own). */
 int moe_pre_expert(const moe_proj_dims* dims, const void* ffn_in, const void* w_packed,
                    const float* w_router, const float* bias, float* logits, void* h_raw,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -297,7 +300,8 @@ int moe_latent_norm(const moe_proj_dims* dims, const void* h_raw, const void* ga
  *            for the bf16 GEMM;
  *   w_packed moe_pack_dense of w_post [N, K] bf16;
  *   out      [S, N] bf16, written: bf16(sum_k bf16(partial[t][k]) w_post[n][k]),
- *            fp32 accumulation as in moe_pre_expert. */
+ *            fp32 accumulation as in moe_pre_expert.
+ * Two launches: the rounding of the partial, then the projection. */
 int moe_post_expert(const moe_proj_dims* dims, const float* partial, const void* w_packed,
                     void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -157,7 +157,8 @@ class ProjSteps:
     """Device buffers of the steps around the block for inputs from
     ``synth.make_proj_inputs``: the pre-expert step (router + pre projection
     of this GPU's rows), the latent norm (on a gathered [S, L] projection) and
-    the post-expert step (this GPU's rows). Allocates only here."""
+    the post-expert step (this GPU's rows). Allocates only in the constructor
+    and in ``add_weight_copies``; ``s`` picks a weight copy."""
 
     def __init__(self, inp: dict, device="cuda"):
         from . import moe_pack_dense, moe_packed_dense_bytes, moe_proj_workspace_bytes, proj_dims_from
@@ -170,34 +171,42 @@ class ProjSteps:
         self.norm_dims = proj_dims_from(dict(S=S, K=L, N=L, eps=pc.eps))
         self.post_dims = proj_dims_from(dict(S=S, K=L, N=pc.n_post))
         self.ffn_in = bf16_tensor(inp["ffn_in"], dv)
-        self.wr = _dev(inp["wr_pre"], dv) if pc.e_router else None
         self.bias = _dev(inp.get("bias_pre"), dv)
-        self.w_pre = torch.empty(moe_packed_dense_bytes(self.pre_dims), dtype=torch.uint8, device=dv)
-        moe_pack_dense(self.pre_dims, bf16_tensor(inp["w_pre"], dv), self.w_pre)
+        w_pre = torch.empty(moe_packed_dense_bytes(self.pre_dims), dtype=torch.uint8, device=dv)
+        moe_pack_dense(self.pre_dims, bf16_tensor(inp["w_pre"], dv), w_pre)
+        w_post = torch.empty(moe_packed_dense_bytes(self.post_dims), dtype=torch.uint8, device=dv)
+        moe_pack_dense(self.post_dims, bf16_tensor(inp["w_post"], dv), w_post)
+        # weight sets: [0] the originals, then copies (add_weight_copies)
+        self.sets = [dict(w_pre=w_pre, wr=_dev(inp["wr_pre"], dv) if pc.e_router else None, w_post=w_post)]
         self.logits = torch.empty((S, max(pc.e_router, 1)), dtype=torch.float32, device=dv)
         self.h_raw = torch.empty((S, pc.n_pre), dtype=torch.bfloat16, device=dv)
-        self.ws_pre = torch.empty(moe_proj_workspace_bytes(self.pre_dims), dtype=torch.uint8, device=dv)
+        # workspaces start zero-filled (their counters); the calls leave them so
+        self.ws_pre = torch.zeros(moe_proj_workspace_bytes(self.pre_dims), dtype=torch.uint8, device=dv)
         self.norm_in = bf16_tensor(inp["h_raw"], dv)
         self.gamma = bf16_tensor(inp.get("gamma_l"), dv)
         self.h = torch.empty((S, L), dtype=torch.bfloat16, device=dv)
         self.partial = _dev(inp["partial"], dv)
-        self.w_post = torch.empty(moe_packed_dense_bytes(self.post_dims), dtype=torch.uint8, device=dv)
-        moe_pack_dense(self.post_dims, bf16_tensor(inp["w_post"], dv), self.w_post)
         self.out = torch.empty((S, pc.n_post), dtype=torch.bfloat16, device=dv)
-        self.ws_post = torch.empty(moe_proj_workspace_bytes(self.post_dims), dtype=torch.uint8, device=dv)
+        self.ws_post = torch.zeros(moe_proj_workspace_bytes(self.post_dims), dtype=torch.uint8, device=dv)
 
-    def pre(self):
+    def add_weight_copies(self, n: int) -> None:
+        """n more copies of the weights, for timing with a cold last-level cache."""
+        for _ in range(n):
+            self.sets.append({k: (None if v is None else v.clone()) for k, v in self.sets[0].items()})
+
+    def pre(self, s=0):
         from . import moe_pre_expert
 
-        moe_pre_expert(self.pre_dims, self.ffn_in, self.w_pre, self.wr, self.bias,
+        st = self.sets[s]
+        moe_pre_expert(self.pre_dims, self.ffn_in, st["w_pre"], st["wr"], self.bias,
                        self.logits if self.pc.e_router else None, self.h_raw, self.ws_pre)
 
-    def norm(self):
+    def norm(self, s=0):
         from . import moe_latent_norm
 
         moe_latent_norm(self.norm_dims, self.norm_in, self.gamma, self.h)
 
-    def post(self):
+    def post(self, s=0):
         from . import moe_post_expert
 
-        moe_post_expert(self.post_dims, self.partial, self.w_post, self.out, self.ws_post)
+        moe_post_expert(self.post_dims, self.partial, self.sets[s]["w_post"], self.out, self.ws_post)

@@ -207,7 +207,8 @@ struct NoWait {
 // before the first activation load; red: LDS. kCoh: the SwiGLU rows pass
 // between workgroups of one launch (gate_up writes them through to the
 // coherence point, down reads them from there). kF32Out (not gate_up): out
-// holds fp32 rows (a split-K partial), written unrounded.
+// holds fp32 rows (a split-K partial), written unrounded through to the
+// coherence point, for another workgroup to sum.
 template <bool kMx, int TTG, int P, bool kGateUp, bool kCoh, bool kF32Out = false, class SrcOf,
           class BeforeB>
 __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int NC,
@@ -303,8 +304,10 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
       else *hp = hv;
     } else if constexpr (kF32Out) {
       const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
-      float* frow = reinterpret_cast<float*>(out) + static_cast<size_t>(row0 + c) * out_ld;
-      *reinterpret_cast<f32x4_t*>(frow + n0) = s;
+      float* frow = reinterpret_cast<float*>(out) + static_cast<size_t>(row0 + c) * out_ld + n0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(frow + i, s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
       *reinterpret_cast<u32x2_t*>(orow + n0) =

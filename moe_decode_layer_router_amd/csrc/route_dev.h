@@ -66,8 +66,22 @@ inline int router_nw(int d) {
   return nf <= kWave ? 1 : nf <= 2 * kWave ? 2 : 4;
 }
 
-// Workgroup-level (kRouteThreads): logits of expert row e for all S tokens.
-// Wave w sums K slice w; lane l takes the float4s l, l + 64, .. (NW of them)
+// Sum of one token's NWV K-slice partials rt[slice][j], as a fixed pairwise
+// tree: (0 + 1), (2 + 3), ..., then pairs of those, down to one value.
+template <int NWV>
+__device__ __forceinline__ float slice_tree(const float (*rt)[kTok], int j) {
+  float q[NWV / 2];
+#pragma unroll
+  for (int i = 0; i < NWV / 2; ++i) q[i] = rt[2 * i][j] + rt[2 * i + 1][j];
+#pragma unroll
+  for (int n = NWV / 4; n >= 1; n >>= 1)
+#pragma unroll
+    for (int i = 0; i < n; ++i) q[i] = q[2 * i] + q[2 * i + 1];
+  return q[0];
+}
+
+// Workgroup-level (NWV waves; kRouteThreads for the router launches): logits
+// of expert row e for all S tokens. Wave w sums K slice w; lane l takes the float4s l, l + 64, .. (NW of them)
 // of the slice. The router row is loaded once, all of it in flight at once
 // (non-temporal: it is read once); activations stream in tiles of 8 tokens
 // (with DB, the next tile's loads issue before the current tile is summed).
@@ -75,15 +89,15 @@ inline int router_nw(int d) {
 // sums: a fixed shuffle tree in the wave into LDS `red` [tile][wave][token]
 // (no barrier between tiles, so the waves stream their tiles independently),
 // then, after one barrier, a fixed pairwise tree over the 16 slices.
-template <int NW, bool DB>
+template <int NW, bool DB, int NWV = kRouteWaves>
 __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
                                            const float* __restrict__ wr,
                                            const float* __restrict__ bias,
                                            float* __restrict__ logits, int S, int d, int E, int e,
-                                           float (*red)[kRouteWaves][kTok]) {
+                                           float (*red)[NWV][kTok]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
-  const int kq = d / kRouteWaves;  // K of one wave
+  const int kq = d / NWV;  // K of one wave
   const int nf = kq / 4;           // its float4s
   const int k0 = w * kq;
   int f[NW];
@@ -138,17 +152,8 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
     }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < S; t += blockDim.x) {
-    const float(*rt)[kTok] = red[t / kTok];
-    const int j = t % kTok;
-    float q[kRouteWaves / 2];
-#pragma unroll
-    for (int i = 0; i < kRouteWaves / 2; ++i) q[i] = rt[2 * i][j] + rt[2 * i + 1][j];
-#pragma unroll
-    for (int i = 0; i < kRouteWaves / 4; ++i) q[i] = q[2 * i] + q[2 * i + 1];
-    const float sum = (q[0] + q[1]) + (q[2] + q[3]);
-    logits[static_cast<size_t>(t) * E + e] = sum + b;
-  }
+  for (int t = threadIdx.x; t < S; t += blockDim.x)
+    logits[static_cast<size_t>(t) * E + e] = slice_tree<NWV>(red[t / kTok], t % kTok) + b;
 }
 
 // Larger S: kRouteBlockTok tokens x NE expert rows a workgroup. Every
@@ -213,14 +218,7 @@ __device__ __forceinline__ void router_block(const uint16_t* __restrict__ x,
     const int t = idx / NE, j = idx - t * NE;
     const int e = e0 + j;
     if (e >= E) continue;
-    const float(*rt)[kTok] = red[(t / kTok) * NE + j];
-    const int q0 = t % kTok;
-    float q[kRouteWaves / 2];
-#pragma unroll
-    for (int i = 0; i < kRouteWaves / 2; ++i) q[i] = rt[2 * i][q0] + rt[2 * i + 1][q0];
-#pragma unroll
-    for (int i = 0; i < kRouteWaves / 4; ++i) q[i] = q[2 * i] + q[2 * i + 1];
-    const float sum = (q[0] + q[1]) + (q[2] + q[3]);
+    const float sum = slice_tree<kRouteWaves>(red[(t / kTok) * NE + j], t % kTok);
     logits[static_cast<size_t>(t0 + t) * E + e] = sum + (bias ? bias[e] : 0.0f);
   }
 }

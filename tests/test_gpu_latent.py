@@ -117,11 +117,14 @@ def test_edge_cases(name):
 
 
 def test_repeated_calls_agree():
+    """Back-to-back calls give the same bytes: the part counters return to
+    zero within every call, and the partials' region may hold anything."""
     inp = make_proj_inputs(_small(S=20), 2)
     st = _steps(inp)
     first = [to_np(t).copy() for t in (st.logits, st.h_raw, st.h, st.out)]
-    st.ws_pre.fill_(0x7F)
-    st.ws_post.fill_(0x7F)
+    for ws, n_out in ((st.ws_pre, st.pc.n_pre), (st.ws_post, st.pc.n_post)):
+        n_part = st.pc.S * n_out * 4  # the first part's partials at least
+        ws[:n_part].fill_(0x7F)
     for _ in range(2):
         st.pre()
         st.norm()
