@@ -17,34 +17,41 @@ namespace moeblk {
 constexpr int kTok = 8;  // tokens a router wave sums at once
 constexpr int kMaxRouteTiles = 128 / kTok;  // S <= 128
 
+// A DPP move of v within rows of 16 lanes (kCtrl: a dpp_ctrl value)
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
 // 8 per-lane partial sums -> wave totals; lane l (l % 8 == 0) holds the total of
 // value index ((l >> 5) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 3) & 1). Each step
-// halves the values a lane keeps; the order of additions is fixed.
+// halves the values a lane keeps, adding a partner lane's: lane bit 5 through
+// v_permlane32_swap (the swap of x's upper half with y's lower half leaves
+// every lane the two addends of the half it keeps), bit 4 through
+// v_permlane16_swap (odd rows with even rows), bit 3 through the DPP row
+// mirror (lane i and 15 - i); then the 8 lanes of a group are summed with the
+// half-row mirror and two quad permutations. No LDS; the order of additions
+// is fixed.
 __device__ __forceinline__ float reduce8(float (&v)[kTok], int lane) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const bool hi = lane & 32;
-    const float send = hi ? v[j] : v[4 + j];
-    const float keep = hi ? v[4 + j] : v[j];
-    v[j] = keep + __shfl_xor(send, 32, kWave);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[4 + j]),
+                                                    false, false);
+    v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const bool hi = lane & 16;
-    const float send = hi ? v[j] : v[2 + j];
-    const float keep = hi ? v[2 + j] : v[j];
-    v[j] = keep + __shfl_xor(send, 16, kWave);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[2 + j]),
+                                                    false, false);
+    v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  {
-    const bool hi = lane & 8;
-    const float send = hi ? v[0] : v[1];
-    const float keep = hi ? v[1] : v[0];
-    v[0] = keep + __shfl_xor(send, 8, kWave);
-  }
-  float s = v[0];
-  s += __shfl_xor(s, 4, kWave);
-  s += __shfl_xor(s, 2, kWave);
-  s += __shfl_xor(s, 1, kWave);
+  const bool hi = lane & 8;
+  const float send = hi ? v[0] : v[1];
+  const float keep = hi ? v[1] : v[0];
+  float s = keep + dpp_move<0x140>(send);  // row mirror: partner 15 - i
+  s += dpp_move<0x141>(s);                 // half-row mirror: 7 - i within 8
+  s += dpp_move<0x4E>(s);                  // quad [2, 3, 0, 1]
+  s += dpp_move<0xB1>(s);                  // quad [1, 0, 3, 2]
   return s;
 }
 
