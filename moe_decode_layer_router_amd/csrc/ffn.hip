@@ -119,6 +119,24 @@ ffn_single_kernel(FfnArgs a) {
                                        WaitFlag{&a.ready[t * kCtlStride], a.error}, red);
 }
 
+// chunks in flight a wave in the single launch for 32-token groups
+#ifndef MOE_BIG_PG
+#define MOE_BIG_PG 2
+#endif
+#ifndef MOE_BIG_PD
+#define MOE_BIG_PD 2
+#endif
+
+// chunks in flight a wave of the routed tasks in the two launches for
+// 32-token groups (measured at S = 128 with the shared expert, FFN us:
+// 1/1 176.0, 1/2 177.4, 1/3 179.1, 2/2 181.5)
+#ifndef MOE_PAIR_PG
+#define MOE_PAIR_PG 1
+#endif
+#ifndef MOE_PAIR_PD
+#define MOE_PAIR_PD 1
+#endif
+
 template <int TTG, int P, bool kShared>
 __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
   __shared__ f32x4_t red[kSplit][kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave];
@@ -245,12 +263,13 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   if (single_launch(m)) {
     const int grid = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
     if (big)
-      hipLaunchKernelGGL((ffn_single_kernel<2, 2, 2>), dim3(grid), dim3(kSplit * kWave), 0, stream, a);
+      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_BIG_PG, MOE_BIG_PD>), dim3(grid), dim3(kSplit * kWave), 0,
+                         stream, a);
     else
       hipLaunchKernelGGL((ffn_single_kernel<1, 2, MOE_SINGLE_PD>), dim3(grid), dim3(kSplit * kWave), 0,
                          stream, a);
   } else {  // a shared expert
-    big ? launch_pair<2, 2, 2, true>(a, stream) : launch_pair<1, 2, 4, true>(a, stream);
+    big ? launch_pair<2, MOE_PAIR_PG, MOE_PAIR_PD, true>(a, stream) : launch_pair<1, 2, 4, true>(a, stream);
   }
   return launch_status();
 }

@@ -8,7 +8,10 @@
 namespace moeblk {
 
 constexpr int kSharedTTG = 2;  // shared expert: 32-token groups
-constexpr int kSharedP = 2;
+#ifndef MOE_SHARED_P
+#define MOE_SHARED_P 2
+#endif
+constexpr int kSharedP = MOE_SHARED_P;
 
 struct FfnArgs {
   const uint8_t* w13;  // packed MXFP4 gate_up of the local experts
