@@ -185,3 +185,29 @@ def test_latent_chain(bias_mode):
     # output's magnitude on top of the plain bound
     bound = 2e-2 * rms + 2.0**-7 * np.abs(ref)
     assert np.all(np.abs(got - ref) <= bound), f"max error {np.abs(got - ref).max():.3g}, rms {rms:.3g}"
+
+
+def _random_proj(seed):
+    """Seeded random sizes inside the supported ranges (small enough for the
+    oracle): S, the input and latent widths, the rows held, router rows, bias
+    mode."""
+    r = np.random.default_rng([seed, 91])
+    return _small(
+        name=f"random{seed}",
+        S=int(r.integers(1, 129)),
+        D=128 * int(r.integers(1, 25)),
+        L=128 * int(r.integers(1, 9)),
+        n_pre=64 * int(r.integers(1, 9)),
+        e_router=int(r.integers(0, 65)),
+        n_post=64 * int(r.integers(1, 9)),
+        bias_mode=int(r.integers(0, 2)),
+    )
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes(seed):
+    pc = _random_proj(seed)
+    inp = make_proj_inputs(pc, 20 + seed)
+    rng = np.random.default_rng(seed)
+    inp["bias_pre"] = (rng.standard_normal(pc.e_router) * 0.3).astype(np.float32) if pc.e_router else None
+    _check_all(inp, _steps(inp))
