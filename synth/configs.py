@@ -133,6 +133,12 @@ CONFIGS = {
     ),
 }
 
+# the K5 page's other row counts on the S = 8 workload's shapes and routing
+for _S in (32, 96):
+    CONFIGS[f"s{_S}_uniform"] = CONFIGS["s8_uniform"].with_(
+        name=f"s{_S}_uniform", S=_S, desc=f"S={_S}, as s8_uniform (uniform routing)"
+    )
+
 # the order the workloads are listed in: tiny first, then S = 8, 16, 64, 128
 CONFIG_ORDER = ["tiny", "s8_uniform", "s16_local25", "s64_zipf", "s128_shared"]
 

@@ -189,7 +189,7 @@ def test_full_workload(name, n_tok):
 def test_more_row_counts(S):
     """The K5 page's other row counts (S = 32, 96) on the S = 8 workload's
     shapes and routing, through both entry points."""
-    cfg = get_config("s8_uniform").with_(name=f"s{S}_uniform", S=S)
+    cfg = get_config(f"s{S}_uniform")
     inp = make_inputs(cfg, 1, gamma="random")
     g = run_gpu(inp)
     check_block(inp, g, tokens=_sample_tokens(g, cfg, 3), strict=True)
