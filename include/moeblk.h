@@ -287,7 +287,9 @@ int moe_pre_expert(const moe_proj_dims* dims, const void* ffn_in, const void* w_
                    const float* w_router, const float* bias, float* logits, void* h_raw,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* pre_expert_norm (K5 page, HA: one token a CTA), on the whole latent:
+/* pre_expert_norm (K5 page, HA: one token a CTA), on the whole latent. It
+ * reads dims->S, dims->N (= L) and dims->eps; the other fields must still be
+ * in range.
  *   h_raw [S, N] bf16 (N = L), gamma [N] bf16 or NULL (ones);
  *   h     [S, N] bf16, written: bf16(h_raw * r * gamma) with
  *         r = (sum_c h_raw[t][c]^2 / N + eps)^(-1/2), evaluated in fp64. */
