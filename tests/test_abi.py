@@ -266,3 +266,53 @@ def test_proj_calls_reject():
     assert _rc("moe_topk", bd, None, None, FAKE, FAKE, None) == mb.MOE_ERR_NULL
     assert _rc("moe_topk", bd, FAKE, MIS, FAKE, FAKE, None) == mb.MOE_ERR_ALIGN
     assert _rc("moe_topk", ctypes.byref(dims(S=0)), FAKE, None, FAKE, FAKE, None) == mb.MOE_ERR_SHAPE
+
+
+def test_forward_rejects():
+    d = dims()
+    need = mb.moe_forward_workspace_bytes(d)
+    assert need == mb.moe_ffn_workspace_bytes(d)
+    # x, w_router, bias, w13, w2, ws13, ws2, gamma, logits, ids, w, counts,
+    # offsets, rows, pick_pos, active, y, out, workspace
+    ok = [FAKE, FAKE, None, FAKE, FAKE, None, None, None] + [FAKE] * 11
+    call = lambda dd, a, n=need: _rc("moe_forward", ctypes.byref(dd), *a, n, None)  # noqa: E731
+    assert call(dims(S=0), ok) == mb.MOE_ERR_SHAPE
+    assert call(dims(bias_mode=3), ok) == mb.MOE_ERR_UNSUPPORTED
+    for i in [0, 1, 3, 4] + list(range(8, 19)):
+        a = list(ok)
+        a[i] = None
+        assert call(d, a) == mb.MOE_ERR_NULL, i
+        a[i] = MIS
+        assert call(d, a) == mb.MOE_ERR_ALIGN, i
+    for i in (2, 5, 6, 7):  # optional pointers: misaligned is still an error
+        a = list(ok)
+        a[i] = MIS
+        assert call(d, a) == mb.MOE_ERR_ALIGN, i
+    assert call(d, ok, need - 1) == mb.MOE_ERR_WORKSPACE
+    d4 = mb.dims_from(CONFIGS["s128_shared"])  # a shared expert needs its weights
+    assert call(d4, ok, mb.moe_forward_workspace_bytes(d4)) == mb.MOE_ERR_NULL
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback: with the library missing, the first call raises."""
+    import subprocess
+    import sys
+
+    code = (
+        "import moe_decode_layer_router_amd as mb\n"
+        f"mb._LIB_PATH = {str(tmp_path / 'missing.so')!r}\n"
+        "try:\n    mb.moe_abi_version()\nexcept RuntimeError as e:\n    print('raised:', e)\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert "raised:" in out.stdout and "is not built" in out.stdout, out.stdout + out.stderr
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 2 and "one GPU" in out.stderr, out.stderr
