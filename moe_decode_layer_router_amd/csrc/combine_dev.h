@@ -101,6 +101,16 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y,
       }
     }
   }
+  // the shared expert's row is loaded now, so that it arrives while the
+  // routed picks are summed
+  u32x4_t shq[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = threadIdx.x + kCombineThreads * i;
+    shq[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (shared_row0 >= 0 && v < nvec)
+      shq[i] = *reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(shared_row0 + t) * d + 8 * v);
+  }
   __amdgpu_buffer_rsrc_t yr;
   if constexpr (kCoh)
     yr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(y), 0, 0x7fffffff, 0x00020000);
@@ -160,13 +170,10 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y,
     const int v = threadIdx.x + kCombineThreads * i;
     if (v >= nvec) continue;
     if (shared_row0 >= 0) {
-      const uint4 q =
-          *reinterpret_cast<const uint4*>(y + static_cast<size_t>(shared_row0 + t) * d + 8 * v);
-      const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[i][2 * j] += bf16_lo(qw[j]);
-        acc[i][2 * j + 1] += bf16_hi(qw[j]);
+        acc[i][2 * j] += bf16_lo(shq[i][j]);
+        acc[i][2 * j + 1] += bf16_hi(shq[i][j]);
       }
     }
     float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * d + 8 * v);
