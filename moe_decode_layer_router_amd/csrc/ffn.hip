@@ -88,10 +88,27 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
 #ifndef MOE_SINGLE_OCC2
 #define MOE_SINGLE_OCC2 3
 #endif
+// 32-row items holding at most 16 bucket rows that fit in kBigLdsB bytes of
+// LDS stage them there (ffn_task_ldsb), with this many weight chunks in flight
+// a wave (gate_up / down; a down task issues them before it waits). The LDS of
+// three workgroups a CU fits.
+constexpr int kBigLdsB = 49152;
+#ifndef MOE_BIG_LDSB_PG
+#define MOE_BIG_LDSB_PG 4
+#endif
+#ifndef MOE_BIG_LDSB_PD
+#define MOE_BIG_LDSB_PD 4
+#endif
 template <int TTG, int PG, int PD>
 __global__ __launch_bounds__(kSplit * kWave, TTG == 1 ? MOE_SINGLE_OCC : MOE_SINGLE_OCC2) void
 ffn_single_kernel(FfnArgs a) {
-  __shared__ f32x4_t red[kSplit][TTG][4][kWave];
+  // LDS: the partial tiles of the reduction; with 32-row items also the B rows
+  // of a task that stages them (ffn_task_ldsb)
+  constexpr int kRedBytes = static_cast<int>(sizeof(f32x4_t)) * kSplit * TTG * 4 * kWave;
+  constexpr int kSmem =
+      TTG == 2 && ldsb_smem<kBigLdsB>() > kRedBytes ? ldsb_smem<kBigLdsB>() : kRedBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  auto red = reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(smem);
   const int lane = threadIdx.x & (kWave - 1);
   const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
   const int n_work = count_work<TTG>(cnt);
@@ -102,8 +119,20 @@ ffn_single_kernel(FfnArgs a) {
   if (t < n_work * RB13) {
     const int wi = t / RB13, rb = t - wi * RB13;
     find_task<TTG>(cnt, wi, el, row0, ntok);
+    el = __builtin_amdgcn_readfirstlane(el);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    ntok = __builtin_amdgcn_readfirstlane(ntok);
     const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB13 + rb) * NC13 * kMxTileBytes;
     const int32_t* rows = a.rows;
+    if constexpr (TTG == 2) {
+      if (ntok <= 16 && ntok * a.d * 2 <= kBigLdsB) {
+        ffn_task_ldsb<MOE_BIG_LDSB_PG, kBigLdsB, true, true>(
+            tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; },
+            NoWait{}, smem);
+        publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
+        return;
+      }
+    }
     ffn_task<true, TTG, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
                                         [rows](int r) { return rows[r]; }, NoWait{}, red);
     publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
@@ -113,7 +142,18 @@ ffn_single_kernel(FfnArgs a) {
   if (t >= n_work * RB2) return;
   const int wi = t / RB2, rb = t - wi * RB2;
   find_task<TTG>(cnt, wi, el, row0, ntok);
+  el = __builtin_amdgcn_readfirstlane(el);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  ntok = __builtin_amdgcn_readfirstlane(ntok);
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB2 + rb) * NC2 * kMxTileBytes;
+  if constexpr (TTG == 2) {
+    if (ntok <= 16 && ntok * a.I * 2 <= kBigLdsB) {
+      ffn_task_ldsb<MOE_BIG_LDSB_PD, kBigLdsB, false, true>(
+          tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d, [](int r) { return r; },
+          WaitFlag{&a.ready[t * kCtlStride], a.error}, smem);
+      return;
+    }
+  }
   ffn_task<true, TTG, PD, false, true>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d,
                                        [](int r) { return r; },
                                        WaitFlag{&a.ready[t * kCtlStride], a.error}, red);
@@ -137,9 +177,30 @@ ffn_single_kernel(FfnArgs a) {
 #define MOE_PAIR_PD 1
 #endif
 
+// Routed tasks of the two launches whose bucket rows fit in kPairLdsB bytes of
+// LDS stage them there (ffn_task_ldsb) and keep this many weight chunks in
+// flight a wave (gate_up / down)
+constexpr int kPairLdsB = 65536;
+#ifndef MOE_PAIR_LDSB_PG
+#define MOE_PAIR_LDSB_PG 6
+#endif
+#ifndef MOE_PAIR_LDSB_PD
+#define MOE_PAIR_LDSB_PD 4
+#endif
+
+// LDS of the two launches: the partial tiles of the reduction, or the B rows
+// of a routed task that stages them
+template <int TTG>
+constexpr int pair_smem() {
+  constexpr int red = static_cast<int>(sizeof(f32x4_t)) * kSplit *
+                      (kSharedTTG > TTG ? kSharedTTG : TTG) * 4 * kWave;
+  return red > ldsb_smem<kPairLdsB>() ? red : ldsb_smem<kPairLdsB>();
+}
+
 template <int TTG, int P, bool kShared>
 __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
-  __shared__ f32x4_t red[kSplit][kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG>()];
+  auto red = reinterpret_cast<f32x4_t(*)[kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave]>(smem);
   const int NC = a.d / kChunkK;
   int t = blockIdx.x;
   if constexpr (kShared) {
@@ -164,8 +225,17 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
   const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
   int el, row0, ntok;
   if (!find_task<TTG>(cnt, wi, el, row0, ntok)) return;
+  el = __builtin_amdgcn_readfirstlane(el);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  ntok = __builtin_amdgcn_readfirstlane(ntok);
   const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
   const int32_t* rows = a.rows;
+  if (ntok <= 16 && ntok * a.d * 2 <= kPairLdsB) {
+    ffn_task_ldsb<MOE_PAIR_LDSB_PG, kPairLdsB, true, false>(
+        tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; }, NoWait{},
+        smem);
+    return;
+  }
   ffn_task<true, TTG, P, true, false>(tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I,
                                       [rows](int r) { return rows[r]; }, NoWait{},
                                       reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
@@ -173,7 +243,8 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
 
 template <int TTG, int P, bool kShared>
 __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
-  __shared__ f32x4_t red[kSplit][kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG>()];
+  auto red = reinterpret_cast<f32x4_t(*)[kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave]>(smem);
   const int RB = a.d / kRowsPerBlock;
   auto same = [](int r) { return r; };
   int t = blockIdx.x;
@@ -199,7 +270,15 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
   const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
   int el, row0, ntok;
   if (!find_task<TTG>(cnt, wi, el, row0, ntok)) return;
+  el = __builtin_amdgcn_readfirstlane(el);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  ntok = __builtin_amdgcn_readfirstlane(ntok);
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
+  if (ntok <= 16 && ntok * a.I * 2 <= kPairLdsB) {
+    ffn_task_ldsb<MOE_PAIR_LDSB_PD, kPairLdsB, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb,
+                                                            a.y, a.d, same, NoWait{}, smem);
+    return;
+  }
   ffn_task<true, TTG, P, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb, a.y, a.d, same,
                                        NoWait{}, reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }

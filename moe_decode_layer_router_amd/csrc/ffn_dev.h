@@ -196,6 +196,58 @@ __device__ __forceinline__ void compute_chunk(const BfChunk<TTG>& ch, f32x4_t (&
     }
 }
 
+// Sum of the 4 waves' partial tiles of a task in wave order, then the
+// epilogue: gate_up rounds gate and up to bf16 and writes SwiGLU rows; down
+// writes bf16 rows; kF32Out writes unrounded fp32 rows. Workgroup-level.
+template <int TTG, bool kGateUp, bool kCoh, bool kF32Out>
+__device__ __forceinline__ void task_epilogue(const f32x4_t (&acc)[TTG][4], int n_tt, int ntok,
+                                              int row0, int rb, uint16_t* __restrict__ out,
+                                              int out_ld, f32x4_t (*red)[TTG][4][kWave]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  // sum the 4 waves' partial tiles in wave order
+  __syncthreads();  // the previous task's epilogue has read red
+#pragma unroll
+  for (int tt = 0; tt < TTG; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[w][tt][r][lane] = acc[tt][r];
+  __syncthreads();
+
+  const int r = w;  // this thread finishes row tile r, MFMA lane `lane`
+#pragma unroll
+  for (int tt = 0; tt < TTG; ++tt) {
+    if (tt >= n_tt) break;
+    f32x4_t s = red[0][tt][r][lane];
+#pragma unroll
+    for (int ww = 1; ww < kSplit; ++ww) s += red[ww][tt][r][lane];
+    const int c = tt * 16 + col;
+    if (c >= ntok) continue;
+    uint16_t* orow = out + static_cast<size_t>(row0 + c) * out_ld;
+    if constexpr (kGateUp) {
+      // rows 4g..4g+3 of tile r: gate i, gate i+1, up i, up i+1
+      const float g0 = round_bf16(s[0]), g1 = round_bf16(s[1]);
+      const float u0 = round_bf16(s[2]), u1 = round_bf16(s[3]);
+      const int i0 = 32 * rb + 8 * r + 2 * g;
+      const uint32_t hv = swiglu_bf16_bits(g0, u0) | (swiglu_bf16_bits(g1, u1) << 16);
+      uint32_t* hp = reinterpret_cast<uint32_t*>(orow + i0);
+      if constexpr (kCoh) __hip_atomic_store(hp, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *hp = hv;
+    } else if constexpr (kF32Out) {
+      const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
+      float* frow = reinterpret_cast<float*>(out) + static_cast<size_t>(row0 + c) * out_ld + n0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(frow + i, s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
+      *reinterpret_cast<u32x2_t*>(orow + n0) =
+          u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+    }
+  }
+}
+
 struct NoWait {
   __device__ void operator()() const {}
 };
@@ -275,45 +327,145 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
   for (int i = 0; i < P; ++i)
     if (j0 + P + i < my_n) compute_chunk<TTG>(ring[i], acc, n_tt);
 
-  // sum the 4 waves' partial tiles in wave order
-  __syncthreads();  // the previous task's epilogue has read red
+  task_epilogue<TTG, kGateUp, kCoh, kF32Out>(acc, n_tt, ntok, row0, rb, out, out_ld, red);
+}
+
+// ---------------------------------------------------------------------------
+// A routed MXFP4 task whose few bucket rows fit in LDS (ntok * K * 2 bytes at
+// most kLdsB): the rows are copied into LDS once, and every MFMA step
+// reads its B operand from there. The register ring then holds weights only
+// (17 VGPRs a chunk instead of 33), so a wave keeps PW weight chunks in flight
+// at the register cost of about PW / 2 chunks of the ring with activations,
+// and the LDS reads wait on their own counter, not behind the weight loads.
+// Items of 32 rows at S > 16 often hold only a few picks: the task then runs
+// one token tile instead of two.
+// Columns past the task's rows read its last row (an LDS broadcast) and are
+// never stored. After the main loop the same LDS holds the partial tiles of
+// the wave-order reduction (task_epilogue).
+
+// LDS of a task that stages its B rows: kLdsB bytes of rows + their sources
+// (32 ints)
+template <int kLdsB>
+constexpr int ldsb_smem() { return kLdsB + 128; }
+
+struct MxW {
+  u32x4_t w[4];  // 4 row tiles x 32 e2m1 codes a lane
+  uint32_t s;    // the 4 row tiles' e8m0 bytes
+};
+
+__device__ __forceinline__ void load_w(MxW& ch, const uint8_t* wlane, const uint8_t* slane, int c) {
+  const uint8_t* t = wlane + static_cast<size_t>(c) * kMxTileBytes;
 #pragma unroll
-  for (int tt = 0; tt < TTG; ++tt)
+  for (int r = 0; r < 4; ++r) ch.w[r] = ld_nt<u32x4_t>(t + r * 1024);
+  ch.s = ld_nt<uint32_t>(slane + static_cast<size_t>(c) * kMxTileBytes);
+}
+
+// lb: this lane's B row in LDS (its token column, + its K group 32 g)
+__device__ __forceinline__ void compute_chunk_ldsb(const MxW& ch, const uint16_t* lb, int c,
+                                                   f32x4_t (&acc)[4]) {
+  u32x4_t b[4];
+  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(lb + c * kChunkK);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[w][tt][r][lane] = acc[tt][r];
+  for (int q = 0; q < 4; ++q) b[q] = p[q];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float sc = e8m0_scale((ch.s >> (8 * r)) & 0xffu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc[r] = mfma_bf16(decode_fp4x8(ch.w[r][q], sc), __builtin_bit_cast(bf16x8_t, b[q]), acc[r]);
+  }
+}
+
+// Workgroup-level, same contract as ffn_task<true, TTG, ., kGateUp, kCoh> for
+// ntok <= 16 and ntok * K * 2 <= kLdsB; smem: ldsb_smem<kLdsB>() bytes of LDS.
+template <int PW, int kLdsB, bool kGateUp, bool kCoh, class SrcOf, class BeforeB>
+__device__ __forceinline__ void ffn_task_ldsb(const uint8_t* __restrict__ tiles, int NC,
+                                              const uint16_t* __restrict__ bsrc, int K, int row0,
+                                              int ntok, int rb, uint16_t* __restrict__ out,
+                                              int out_ld, SrcOf src_of, BeforeB before_b,
+                                              uint8_t* smem) {
+  constexpr int kThreads = kSplit * kWave;
+  constexpr int kPer = kLdsB / 16 / kThreads;  // 16-byte pieces a thread copies, at most
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  uint16_t* lds_b = reinterpret_cast<uint16_t*>(smem);
+  int* srow = reinterpret_cast<int*>(smem + kLdsB);
+
+  // the rows' sources first: waiting for them leaves the weights in flight
+  int src = 0;
+  if (threadIdx.x < ntok) src = src_of(row0 + threadIdx.x);
+
+  const uint8_t* wlane = tiles + lane * 16;
+  const uint8_t* slane = tiles + 4096 + lane * 4;
+  const int my_n = (NC - w + kSplit - 1) / kSplit;  // this wave's chunks: w, w + 4, ...
+  MxW ring[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) load_w(ring[i], wlane, slane, min(w + kSplit * i, NC - 1));
+
+  if (threadIdx.x < ntok) srow[threadIdx.x] = src;
+  before_b();
   __syncthreads();
 
-  const int r = w;  // this thread finishes row tile r, MFMA lane `lane`
+  // copy the ntok rows (K bf16 each) into LDS, row r at r * K
+  const int pieces = K / 8;
+  const int total = ntok * pieces;
+  constexpr bool kCohB = kCoh && !kGateUp;  // SwiGLU rows of this launch
+  u32x4_t v[kPer];
+  __amdgpu_buffer_rsrc_t rsrc;
+  if constexpr (kCohB)
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(bsrc), 0, 0x7fffffff, 0x00020000);
 #pragma unroll
-  for (int tt = 0; tt < TTG; ++tt) {
-    if (tt >= n_tt) break;
-    f32x4_t s = red[0][tt][r][lane];
-#pragma unroll
-    for (int ww = 1; ww < kSplit; ++ww) s += red[ww][tt][r][lane];
-    const int c = tt * 16 + col;
-    if (c >= ntok) continue;
-    uint16_t* orow = out + static_cast<size_t>(row0 + c) * out_ld;
-    if constexpr (kGateUp) {
-      // rows 4g..4g+3 of tile r: gate i, gate i+1, up i, up i+1
-      const float g0 = round_bf16(s[0]), g1 = round_bf16(s[1]);
-      const float u0 = round_bf16(s[2]), u1 = round_bf16(s[3]);
-      const int i0 = 32 * rb + 8 * r + 2 * g;
-      const uint32_t hv = swiglu_bf16_bits(g0, u0) | (swiglu_bf16_bits(g1, u1) << 16);
-      uint32_t* hp = reinterpret_cast<uint32_t*>(orow + i0);
-      if constexpr (kCoh) __hip_atomic_store(hp, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else *hp = hv;
-    } else if constexpr (kF32Out) {
-      const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
-      float* frow = reinterpret_cast<float*>(out) + static_cast<size_t>(row0 + c) * out_ld + n0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(frow + i, s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
-      *reinterpret_cast<u32x2_t*>(orow + n0) =
-          u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+  for (int i = 0; i < kPer; ++i) {
+    const int q = i * kThreads + threadIdx.x;
+    if (q < total) {
+      const int r = q / pieces, p = q - r * pieces;
+      const uint32_t e = static_cast<uint32_t>(srow[r]) * K + 8 * p;  // element offset
+      if constexpr (kCohB)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, e * 2u, 0, kCpolSc1);
+      else
+        v[i] = *reinterpret_cast<const u32x4_t*>(bsrc + e);
     }
   }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = i * kThreads + threadIdx.x;
+    if (q < total) *reinterpret_cast<u32x4_t*>(lds_b + 8 * q) = v[i];
+  }
+  __syncthreads();
+
+  const uint16_t* lb = lds_b + min(col, ntok - 1) * K + 32 * g;
+  f32x4_t acc[1][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[0][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  int j0 = 0;
+  for (; j0 + 2 * PW <= my_n; j0 += PW) {  // steady state: every refill is needed
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      compute_chunk_ldsb(ring[i], lb, w + kSplit * (j0 + i), acc[0]);
+      load_w(ring[i], wlane, slane, w + kSplit * (j0 + i + PW));
+      // keep each refill right after its chunk: the scheduler would otherwise
+      // sink all PW refills to the end of the iteration and drain the ring
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {  // fewer than 2 PW chunks left
+    if (j0 + i < my_n) {
+      compute_chunk_ldsb(ring[i], lb, w + kSplit * (j0 + i), acc[0]);
+      if (j0 + i + PW < my_n) load_w(ring[i], wlane, slane, w + kSplit * (j0 + i + PW));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PW; ++i)
+    if (j0 + PW + i < my_n) compute_chunk_ldsb(ring[i], lb, w + kSplit * (j0 + PW + i), acc[0]);
+
+  // the barrier at the start of the epilogue ends every wave's B reads before
+  // the partial tiles overwrite them
+  task_epilogue<1, kGateUp, kCoh, false>(acc, 1, ntok, row0, rb, out, out_ld,
+                                         reinterpret_cast<f32x4_t(*)[1][4][kWave]>(smem));
 }
 
 }  // namespace moeblk
