@@ -90,8 +90,10 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
 #endif
 // 32-row items holding at most 16 bucket rows that fit in kBigLdsB bytes of
 // LDS stage them there (ffn_task_ldsb), with this many weight chunks in flight
-// a wave (gate_up / down; a down task issues them before it waits). The LDS of
-// three workgroups a CU fits.
+// a wave (gate_up / down), all issued before the row copy (a down task: before
+// it waits). The LDS of three workgroups a CU fits. Measured FFN us at S = 32
+// / 96: 4 chunks 44.2 / 66.3, 3 chunks 44.2 / 67.0, 5 chunks 45.4 / 67.4; the
+// row copy after the first chunk 44.7 / 67.2.
 constexpr int kBigLdsB = 49152;
 #ifndef MOE_BIG_LDSB_PG
 #define MOE_BIG_LDSB_PG 4
@@ -126,7 +128,7 @@ ffn_single_kernel(FfnArgs a) {
     const int32_t* rows = a.rows;
     if constexpr (TTG == 2) {
       if (ntok <= 16 && ntok * a.d * 2 <= kBigLdsB) {
-        ffn_task_ldsb<MOE_BIG_LDSB_PG, kBigLdsB, true, true>(
+        ffn_task_ldsb<MOE_BIG_LDSB_PG, MOE_BIG_LDSB_PG, kBigLdsB, true, true>(
             tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; },
             NoWait{}, smem);
         publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
@@ -148,7 +150,7 @@ ffn_single_kernel(FfnArgs a) {
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB2 + rb) * NC2 * kMxTileBytes;
   if constexpr (TTG == 2) {
     if (ntok <= 16 && ntok * a.I * 2 <= kBigLdsB) {
-      ffn_task_ldsb<MOE_BIG_LDSB_PD, kBigLdsB, false, true>(
+      ffn_task_ldsb<MOE_BIG_LDSB_PD, MOE_BIG_LDSB_PD, kBigLdsB, false, true>(
           tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d, [](int r) { return r; },
           WaitFlag{&a.ready[t * kCtlStride], a.error}, smem);
       return;
@@ -179,10 +181,12 @@ ffn_single_kernel(FfnArgs a) {
 
 // Routed tasks of the two launches whose bucket rows fit in kPairLdsB bytes of
 // LDS stage them there (ffn_task_ldsb) and keep this many weight chunks in
-// flight a wave (gate_up / down)
+// flight a wave (gate_up / down); the row copy goes out after the first chunk
+// (measured at S = 128 with the shared expert, FFN us: first chunk 162.6,
+// all 6 chunks 168.7; 4 / 6 / 8 chunks 161.8 / 162.6 / 164.3)
 constexpr int kPairLdsB = 65536;
 #ifndef MOE_PAIR_LDSB_PG
-#define MOE_PAIR_LDSB_PG 6
+#define MOE_PAIR_LDSB_PG 4
 #endif
 #ifndef MOE_PAIR_LDSB_PD
 #define MOE_PAIR_LDSB_PD 4
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
   const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
   const int32_t* rows = a.rows;
   if (ntok <= 16 && ntok * a.d * 2 <= kPairLdsB) {
-    ffn_task_ldsb<MOE_PAIR_LDSB_PG, kPairLdsB, true, false>(
+    ffn_task_ldsb<MOE_PAIR_LDSB_PG, 1, kPairLdsB, true, false>(
         tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; }, NoWait{},
         smem);
     return;
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
   ntok = __builtin_amdgcn_readfirstlane(ntok);
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
   if (ntok <= 16 && ntok * a.I * 2 <= kPairLdsB) {
-    ffn_task_ldsb<MOE_PAIR_LDSB_PD, kPairLdsB, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb,
+    ffn_task_ldsb<MOE_PAIR_LDSB_PD, 1, kPairLdsB, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb,
                                                             a.y, a.d, same, NoWait{}, smem);
     return;
   }

@@ -378,7 +378,11 @@ __device__ __forceinline__ void compute_chunk_ldsb(const MxW& ch, const uint16_t
 
 // Workgroup-level, same contract as ffn_task<true, TTG, ., kGateUp, kCoh> for
 // ntok <= 16 and ntok * K * 2 <= kLdsB; smem: ldsb_smem<kLdsB>() bytes of LDS.
-template <int PW, int kLdsB, bool kGateUp, bool kCoh, class SrcOf, class BeforeB>
+// The first kPre weight chunks of a wave are issued before before_b() and the
+// row copy, the rest after the copy's loads: vector loads complete in issue
+// order, so the copy then waits for kPre chunks only (a down task that waits
+// for its flag issues all PW chunks first).
+template <int PW, int kPre, int kLdsB, bool kGateUp, bool kCoh, class SrcOf, class BeforeB>
 __device__ __forceinline__ void ffn_task_ldsb(const uint8_t* __restrict__ tiles, int NC,
                                               const uint16_t* __restrict__ bsrc, int K, int row0,
                                               int ntok, int rb, uint16_t* __restrict__ out,
@@ -400,9 +404,10 @@ __device__ __forceinline__ void ffn_task_ldsb(const uint8_t* __restrict__ tiles,
   const uint8_t* wlane = tiles + lane * 16;
   const uint8_t* slane = tiles + 4096 + lane * 4;
   const int my_n = (NC - w + kSplit - 1) / kSplit;  // this wave's chunks: w, w + 4, ...
+  static_assert(kPre >= 1 && kPre <= PW, "chunks issued before the row copy");
   MxW ring[PW];
 #pragma unroll
-  for (int i = 0; i < PW; ++i) load_w(ring[i], wlane, slane, min(w + kSplit * i, NC - 1));
+  for (int i = 0; i < kPre; ++i) load_w(ring[i], wlane, slane, min(w + kSplit * i, NC - 1));
 
   if (threadIdx.x < ntok) srow[threadIdx.x] = src;
   before_b();
@@ -428,6 +433,10 @@ __device__ __forceinline__ void ffn_task_ldsb(const uint8_t* __restrict__ tiles,
         v[i] = *reinterpret_cast<const u32x4_t*>(bsrc + e);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // the row loads go out before the later chunks
+#pragma unroll
+  for (int i = kPre; i < PW; ++i) load_w(ring[i], wlane, slane, min(w + kSplit * i, NC - 1));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int q = i * kThreads + threadIdx.x;
