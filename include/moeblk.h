@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOEBLK_ABI_VERSION 2 /* 2: moe_dims.bias_mode */
+#define MOEBLK_ABI_VERSION 3 /* 2: moe_dims.bias_mode; 3: moe_route workspace */
 
 /* status codes */
 #define MOE_OK 0
@@ -130,6 +130,11 @@ int moe_pack_bf16(const moe_dims* dims, int which, const void* w, void* packed,
 /* the block                                                                 */
 /* ------------------------------------------------------------------------ */
 
+/* Bytes of scratch moe_route needs: 0 for S <= 32; beyond, the router's
+ * tiles split K into parts whose partial logits ([parts, S, E] fp32) the
+ * top-k launch sums. 0 also if `dims` is invalid. */
+size_t moe_route_workspace_bytes(const moe_dims* dims);
+
 /* Router logits and top-k (K3 page stages "A" and "route"; K5 page, HA).
  *   x        [S, d] bf16 activations;
  *   w_router [E, d] fp32; bias [E] fp32 or NULL (bias_mode 0: added to the
@@ -141,9 +146,17 @@ int moe_pack_bf16(const moe_dims* dims, int which, const void* w, void* packed,
  *            equal keys to the lower id; the key is the logit, or under
  *            bias_mode 1 the fp32 sum logit + bias[e];
  *   topk_w   [S, topk] fp32, written: sigmoid(logit), divided by the sum over
- *            the token's topk picks when renorm = 1. */
+ *            the token's topk picks when renorm = 1;
+ *   workspace device scratch of at least moe_route_workspace_bytes (may be
+ *            NULL when that is 0), caller-owned, no initial contents needed;
+ *            calls sharing it must not overlap.
+ * The fp32 sums run in a fixed order (deterministic): for S <= 32 each of
+ * 1024 threads sums d / 1024 products and a fixed tree adds the threads'
+ * sums; beyond, 16-K blocks of MFMA products go round-robin to 4 chains a
+ * K part, added pairwise, and the parts are added in a fixed order. */
 int moe_route(const moe_dims* dims, const void* x, const float* w_router, const float* bias,
-              float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
+              float* logits, int32_t* topk_ids, float* topk_w, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
 
 /* Bucketing of the local picks (K3 page stage "route"; "dn_loads": expert
  * table etab and count nv), deterministic, no atomics on the output.
@@ -214,8 +227,8 @@ int moe_combine(const moe_dims* dims, const void* y, const float* topk_w, const 
 /* the whole block in one call                                               */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of scratch moe_forward needs (as for moe_expert_ffn); 0 if `dims` is
- * invalid. */
+/* Bytes of scratch moe_forward needs: moe_route's, then moe_expert_ffn's; 0
+ * if `dims` is invalid. */
 size_t moe_forward_workspace_bytes(const moe_dims* dims);
 
 /* The whole block -- the work of moe_route, moe_bucket, moe_expert_ffn and

@@ -27,6 +27,7 @@ __all__ = [
     "moe_packed_bf16_bytes",
     "moe_pack_bf16",
     "moe_route",
+    "moe_route_workspace_bytes",
     "moe_bucket",
     "moe_ffn_workspace_bytes",
     "moe_expert_ffn",
@@ -59,7 +60,7 @@ MOE_W2 = 1
 
 
 # the layout of moe_dims and the entry points below (MOEBLK_ABI_VERSION)
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class MoeDims(ctypes.Structure):
@@ -131,7 +132,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
         L.moe_pack_mxfp4.argtypes = [_DP, ctypes.c_int, _P, _P, _P, _P]
         L.moe_pack_bf16.argtypes = [_DP, ctypes.c_int, _P, _P, _P]
-        L.moe_route.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_route_workspace_bytes.argtypes = [_DP]
+        L.moe_route_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_route.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_bucket.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P]
         L.moe_expert_ffn.argtypes = [_DP] + [_P] * 11 + [ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [_DP, _P, _P, _P, _P, _P, _P]
@@ -236,10 +239,17 @@ def moe_pack_bf16(dims, which, w, packed, stream=None) -> None:
     _call("moe_pack_bf16", ctypes.byref(_d(dims)), int(which), _ptr(w), _ptr(packed), _stream(stream))
 
 
-def moe_route(dims, x, w_router, bias, logits, topk_ids, topk_w, stream=None) -> None:
+def moe_route_workspace_bytes(dims) -> int:
+    return int(lib().moe_route_workspace_bytes(ctypes.byref(_d(dims))))
+
+
+def moe_route(dims, x, w_router, bias, logits, topk_ids, topk_w, workspace=None, stream=None) -> None:
+    """``workspace``: a device tensor of at least moe_route_workspace_bytes
+    (None when that is 0)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call(
         "moe_route", ctypes.byref(_d(dims)), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits),
-        _ptr(topk_ids), _ptr(topk_w), _stream(stream),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(workspace), ctypes.c_size_t(nbytes), _stream(stream),
     )
 
 

@@ -27,6 +27,7 @@ from . import (
     moe_packed_bf16_bytes,
     moe_packed_mxfp4_bytes,
     moe_route,
+    moe_route_workspace_bytes,
 )
 
 
@@ -98,6 +99,8 @@ class MoeBlock:
         self.out = torch.empty((S, d), dtype=torch.float32, device=dv)
         # workspaces: zero-filled once (the calls keep their counters at zero)
         self.ws = torch.zeros(max(moe_ffn_workspace_bytes(self.dims), 16), dtype=torch.uint8, device=dv)
+        rw = moe_route_workspace_bytes(self.dims)
+        self.rws = torch.empty(rw, dtype=torch.uint8, device=dv) if rw else None
         self.fws = torch.zeros(max(moe_forward_workspace_bytes(self.dims), 16), dtype=torch.uint8, device=dv)
 
     def add_weight_copies(self, n: int) -> None:
@@ -108,7 +111,7 @@ class MoeBlock:
     # the four calls -----------------------------------------------------
     def route(self, s=0):
         st = self.sets[s]
-        moe_route(self.dims, self.x, st["wr"], st["bias"], self.logits, self.ids, self.w)
+        moe_route(self.dims, self.x, st["wr"], st["bias"], self.logits, self.ids, self.w, self.rws)
 
     def bucket(self):
         moe_bucket(self.dims, self.ids, self.counts, self.offsets, self.rows, self.pick_pos, self.active)

@@ -1,9 +1,12 @@
 // forward.hip -- moe_forward: the whole block as a chain of launches on one
 // stream.
 //
-//   1  router logits (one workgroup an expert row)
+//   1  router logits (S <= 16: one workgroup an expert row; S <= 32: 16
+//      tokens x a few rows a workgroup; beyond: tiles split over K, their
+//      parts in the workspace)
 //   2  top-k of every token and the bucketing, in one workgroup (S <= 16;
-//      beyond, one wave a token in its own launch, then the bucketing)
+//      beyond, one wave a token in its own launch -- for S > 32 one workgroup
+//      a token that first sums the router parts -- then the bucketing)
 //   3  the expert FFNs (ffn.hip: one launch, or two with a shared expert)
 //   4  per-pick RMSNorm and the weighted sum (one workgroup a token)
 //
@@ -61,9 +64,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
 
 using namespace moeblk;
 
+// workspace: the router's K parts (S > 32), then the FFN's layout (its error
+// word stays last)
 extern "C" size_t moe_forward_workspace_bytes(const moe_dims* dims) {
   if (check_dims(dims)) return 0;
-  return ffn_layout(*dims).total;
+  return router_parts_bytes(*dims) + ffn_layout(*dims).total;
 }
 
 extern "C" int moe_forward(const moe_dims* dims, const void* x, const float* w_router,
@@ -90,17 +95,20 @@ extern "C" int moe_forward(const moe_dims* dims, const void* x, const float* w_r
               MOE_ERR_ALIGN);
   MOE_REQUIRE(workspace_bytes >= moe_forward_workspace_bytes(dims), MOE_ERR_WORKSPACE);
 
-  launch_router_logits(m, x, w_router, bias, logits, stream);
+  const size_t parts_bytes = router_parts_bytes(m);
+  float* parts = parts_bytes ? static_cast<float*>(workspace) : nullptr;
+  void* ffn_ws = static_cast<uint8_t*>(workspace) + parts_bytes;
+  launch_router_logits(m, x, w_router, bias, logits, stream, parts);
   if (m.S <= kTopkThreads / kWave) {
     hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits,
                        select_bias(m, bias), topk_ids, topk_w, counts, offsets, rows, pick_pos, active, m.S, m.E, m.topk, m.renorm,
                        m.n_local, m.local_base, r_max(m));
   } else {  // a wave a token needs more waves than one workgroup holds
-    launch_topk(m, logits, bias, topk_ids, topk_w, stream);
+    launch_topk(m, logits, bias, topk_ids, topk_w, stream, parts, logits);
     launch_bucket(m, topk_ids, counts, offsets, rows, pick_pos, active, stream);
   }
   const int frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y,
-                             workspace, stream);
+                             ffn_ws, stream);
   if (frc) return frc;
   launch_combine(m, y, topk_w, pick_pos, gamma, out, stream);
   return launch_status();

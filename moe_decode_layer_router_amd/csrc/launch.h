@@ -15,11 +15,35 @@ inline const float* select_bias(const moe_dims& m, const float* bias) {
   return m.bias_mode == 1 ? bias : nullptr;
 }
 
-// the router (applies logit_bias itself) and the top-k (select_bias)
+// Router for S > kRouteSplitMinS with scratch: tiles of router_tile_tok(S)
+// tokens x 64 router rows, K split into router_parts(m) parts (a power of two
+// up to 32 that divides d / 16, so that the tiles times the parts stay within
+// 256 workgroups); 0 parts below (no scratch). Router + top-k measured on
+// MI355X, us, whole-K workgroups against split tiles: S = 32 10.2 / 10.7,
+// S = 64 13.4 / 11.4, S = 96 18.7 / 14.9, S = 128 (d = 7168) 27.1 / 18.0.
+constexpr int kRouteSplitMinS = 32;
+inline int router_tile_tok(int S) { return S <= 64 ? 32 : 64; }
+inline int router_parts(const moe_dims& m) {
+  if (m.S <= kRouteSplitMinS) return 0;
+  const int TT = router_tile_tok(m.S);
+  const int tiles = ((m.S + TT - 1) / TT) * ((m.E + 63) / 64);
+  int P = 1;
+  while (P < 32 && tiles * P * 2 <= 256 && (m.d / 16) % (2 * P) == 0) P *= 2;  // <= kMaxRouteParts
+  return P;
+}
+// scratch of the split router: parts [P][S][E] fp32
+inline size_t router_parts_bytes(const moe_dims& m) {
+  return round_up(static_cast<size_t>(router_parts(m)) * m.S * m.E * 4, 256);
+}
+
+// the router (applies logit_bias itself) and the top-k (select_bias). With
+// `parts` (router_parts_bytes of scratch) and S > 16 the router writes its K
+// parts there and the top-k sums them into `logits`; without, the router
+// writes `logits` itself.
 void launch_router_logits(const moe_dims& m, const void* x, const float* wr, const float* bias,
-                          float* logits, hipStream_t stream);
+                          float* logits, hipStream_t stream, float* parts = nullptr);
 void launch_topk(const moe_dims& m, const float* logits, const float* bias, int32_t* ids, float* w,
-                 hipStream_t stream);
+                 hipStream_t stream, const float* parts = nullptr, float* logits_out = nullptr);
 void launch_bucket(const moe_dims& m, const int32_t* ids, int32_t* counts, int32_t* offsets,
                    int32_t* rows, int32_t* pick_pos, int32_t* active, hipStream_t stream);
 // dense bf16 [N][K] -> the bf16 tile order (the down-projection row order)

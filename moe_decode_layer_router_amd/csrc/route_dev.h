@@ -301,12 +301,14 @@ __device__ __forceinline__ void order2(uint32_t& ka, int& ia, float& la, uint32_
 // ordering.
 // ids_lds: if not NULL, the ids are also written there ([t * topk + slot]);
 // mark(id, t) runs for each of the token's ids (lanes < topk).
+// topk_token_vals: the same with the token's logits already in registers
+// (lane l: lv[j] = logit of expert l + 64 j, any value for ids >= E).
 template <bool kSel, class Mark>
-__device__ __forceinline__ void topk_token(const float* __restrict__ logits,
-                                           const float* __restrict__ sel_bias,
-                                           int32_t* __restrict__ ids, float* __restrict__ w,
-                                           int32_t* ids_lds, int E, int topk, int renorm, int t,
-                                           Mark mark) {
+__device__ __forceinline__ void topk_token_vals(const float (&lv)[4],
+                                                const float* __restrict__ sel_bias,
+                                                int32_t* __restrict__ ids, float* __restrict__ w,
+                                                int32_t* ids_lds, int E, int topk, int renorm,
+                                                int t, Mark mark) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t k[4];
   int id[4];
@@ -314,8 +316,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + kWave * j;
-    const float* p = logits + static_cast<size_t>(t) * E + e;
-    lg[j] = e < E ? *p : 0.0f;
+    lg[j] = e < E ? lv[j] : 0.0f;
     if constexpr (kSel) k[j] = e < E ? order_key(lg[j] + sel_bias[e]) : 0u;
     else k[j] = e < E ? order_key(lg[j]) : 0u;  // 0: below every expert
     id[j] = e;
@@ -388,6 +389,204 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
     mark(my_id, t);
     w[static_cast<size_t>(t) * topk + lane] = renorm ? sc / sum : sc;
   }
+}
+
+template <bool kSel, class Mark>
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits,
+                                           const float* __restrict__ sel_bias,
+                                           int32_t* __restrict__ ids, float* __restrict__ w,
+                                           int32_t* ids_lds, int E, int topk, int renorm, int t,
+                                           Mark mark) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float lv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + kWave * j;
+    lv[j] = e < E ? logits[static_cast<size_t>(t) * E + e] : 0.0f;
+  }
+  topk_token_vals<kSel>(lv, sel_bias, ids, w, ids_lds, E, topk, renorm, t, mark);
+}
+
+// ---------------------------------------------------------------------------
+// Router logits for S > 32 as a tiled product split over K, on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32: A = 16 router rows x 4 K, B = 4 K x 16 tokens).
+//
+// A workgroup of 4 waves owns TT tokens x 64 router rows over one K part of
+// Kp: part p covers K [p Kp, (p + 1) Kp). It writes its tile unreduced to
+// parts[p][t][e]; the top-k launch sums the parts in a fixed order. Tiles of
+// TT x 64 load 2 / 64 + 4 / TT bytes per product, against 2 / NE + 4 / 16 for
+// the 16-token x NE-row workgroups that take the whole K, and the K split
+// keeps every CU busy.
+//
+// Wave w takes tokens (w & 1) TT / 2 .. + TT / 2 and rows (w >> 1) 32 .. + 32:
+// NT = TT / 32 token tiles x 2 row tiles of 16 x 16. In a 16-K block a lane
+// loads 4 consecutive K of one router row (16 B) and of one token row (4
+// bf16); MFMA step s takes K index 4 (lane / 16) + s of the block in both
+// operands, so every product of the block is summed once. Block b accumulates
+// into set b % 4; the sets are added as (0 + 1) + (2 + 3), which keeps the
+// sequential chains a quarter of the part. Rows past E and tokens past S
+// repeat the last one and are not stored.
+constexpr int kRouteTileE = 64;
+#ifndef MOE_ROUTE_RING
+#define MOE_ROUTE_RING 8
+#endif
+constexpr int kRouteRing = MOE_ROUTE_RING;  // 16-K blocks in flight a wave
+constexpr int kMaxRouteParts = 32;          // K parts of the split router, at most
+
+template <int NT>
+struct RouteBlk {
+  f32x4_t w[2];   // 2 row tiles: 4 K of this lane's row
+  uint2 x[NT];    // NT token tiles: 4 bf16 of this lane's token
+};
+
+template <int NT>
+__device__ __forceinline__ void route_blk_load(RouteBlk<NT>& b, const float* const (&wrow)[2],
+                                               const uint16_t* const (&xrow)[NT], int blk) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b.w[i] = *reinterpret_cast<const f32x4_t*>(wrow[i] + 16 * blk);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) b.x[j] = *reinterpret_cast<const uint2*>(xrow[j] + 16 * blk);
+}
+
+template <int NT>
+__device__ __forceinline__ void route_blk_mfma(const RouteBlk<NT>& b, f32x4_t (&acc)[2][NT]) {
+  float xf[NT][4];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    xf[j][0] = bf16_lo(b.x[j].x);
+    xf[j][1] = bf16_hi(b.x[j].x);
+    xf[j][2] = bf16_lo(b.x[j].y);
+    xf[j][3] = bf16_hi(b.x[j].y);
+  }
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.w[i][st], xf[j][st], acc[i][j], 0, 0, 0);
+}
+
+// Workgroup (4 waves): tile (tt, et) of K part p.
+template <int TT>
+__device__ __forceinline__ void router_split_tile(const uint16_t* __restrict__ x,
+                                                  const float* __restrict__ wr,
+                                                  float* __restrict__ parts, int S, int d, int E,
+                                                  int Kp, int tt, int et, int p) {
+  constexpr int NT = TT / 32;
+  constexpr int R = kRouteRing;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int t0 = tt * TT + (w & 1) * (TT / 2);
+  const int e0 = et * kRouteTileE + (w >> 1) * 32;
+  const int k0 = p * Kp + 4 * g;
+  const float* wrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    wrow[i] = wr + static_cast<size_t>(min(e0 + 16 * i + c, E - 1)) * d + k0;
+  const uint16_t* xrow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    xrow[j] = x + static_cast<size_t>(min(t0 + 16 * j + c, S - 1)) * d + k0;
+
+  f32x4_t acc[4][2][NT];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[a][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nb = Kp / 16;
+  RouteBlk<NT> ring[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) route_blk_load(ring[i], wrow, xrow, min(i, nb - 1));
+  static_assert(R % 4 == 0, "block b goes to set b % 4");
+  int b0 = 0;  // a multiple of R: block b0 + i goes to set i % 4
+  for (; b0 + 2 * R <= nb; b0 += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      route_blk_mfma(ring[i], acc[i % 4]);
+      route_blk_load(ring[i], wrow, xrow, b0 + i + R);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (b0 + i < nb) {
+      route_blk_mfma(ring[i], acc[i % 4]);
+      if (b0 + i + R < nb) route_blk_load(ring[i], wrow, xrow, b0 + i + R);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (b0 + R + i < nb) route_blk_mfma(ring[i], acc[i % 4]);
+
+  // lane holds rows e0 + 16 i + 4 g + r of token t0 + 16 j + c
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int t = t0 + 16 * j + c;
+    if (t >= S) continue;
+    float* prow = parts + (static_cast<size_t>(p) * S + t) * E;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f32x4_t v = (acc[0][i][j] + acc[1][i][j]) + (acc[2][i][j] + acc[3][i][j]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 16 * i + 4 * g + r;
+        if (e < E) prow[e] = v[r];
+      }
+    }
+  }
+}
+
+// Workgroup (4 waves, kWave * 4 threads): logits of token t = the sum of its
+// KP parts (wave w adds the parts w, w + 4, ... in order; then (0 + 1) +
+// (2 + 3)) + bias, written to logits[t]; then wave 0 takes its top-k.
+template <bool kSel>
+__device__ __forceinline__ void topk_parts_token(const float* __restrict__ parts, int KP,
+                                                 const float* __restrict__ lbias,
+                                                 const float* __restrict__ sel_bias,
+                                                 float* __restrict__ logits,
+                                                 int32_t* __restrict__ ids, float* __restrict__ w,
+                                                 int S, int E, int topk, int renorm, int t,
+                                                 float (*red)[4][kWave]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  // every load of the wave's parts in flight at once, then the adds in order
+  constexpr int kPartsAWave = kMaxRouteParts / 4;
+  float v[kPartsAWave][4];
+#pragma unroll
+  for (int q = 0; q < kPartsAWave; ++q) {
+    const int p = wv + 4 * q;
+    const float* pr = parts + (static_cast<size_t>(min(p, KP - 1)) * S + t) * E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = min(lane + kWave * j, E - 1);
+      v[q][j] = pr[e];
+    }
+  }
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < kPartsAWave; ++q)
+    if (wv + 4 * q < KP)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j] += v[q][j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[wv][j][lane] = s[j];
+  __syncthreads();
+  if (wv != 0) return;
+  float lv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + kWave * j;
+    lv[j] = (red[0][j][lane] + red[1][j][lane]) + (red[2][j][lane] + red[3][j][lane]);
+    if (e < E) {
+      if (lbias) lv[j] += lbias[e];
+      logits[static_cast<size_t>(t) * E + e] = lv[j];
+    }
+  }
+  topk_token_vals<kSel>(lv, sel_bias, ids, w, nullptr, E, topk, renorm, t, NoMark{});
 }
 
 }  // namespace moeblk

@@ -4,9 +4,11 @@ same inputs, compare step by step.
 Tolerances (derived from the arithmetic; every comparison states its own):
 
 * router logits, with u = 2^-24, checked against n u sum_j |x_j w_ej| + u |logit|
-  where n bounds the roundings on any path of the GPU's summation tree: a
-  per-lane loop of at most d / 256 terms, a 6-level shuffle tree, 4 levels
-  over the 16 K slices and the bias add, n = d / 256 + 12;
+  where n bounds the roundings on any path of the GPU's summation order
+  (logit_roundings): for S <= 16 a per-lane loop of at most d / 256 terms, a
+  6-level shuffle tree, 4 levels over the 16 K slices and the bias add,
+  n = d / 256 + 12 (S <= 32); beyond, the MFMA chains of a K part, the parts
+  and the bias;
 * top-k: ids bit-exact, except where the oracle's ranking keys (the logits,
   or logit + bias under the selection-only bias) of the two experts that
   trade places differ by < 1e-5 (several answers are then correct); weights within 1e-6 relative of the oracle's weights computed
@@ -27,6 +29,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import moe_decode_layer_router_amd as mb
 import oracle
 from moe_decode_layer_router_amd.block import MoeBlock
 from tests._ref import bf16_val
@@ -57,13 +60,29 @@ def run_gpu(inp: dict, blk: MoeBlock | None = None, fused: bool = False) -> dict
     )
 
 
+def logit_roundings(cfg, dims) -> float:
+    """Worst-case number of fp32 roundings on the way to one GPU logit, from the
+    summation order moe_route documents (the pages fix fp32 accumulation, not
+    an order). Without scratch (S <= 32): a thread sums d / 1024 products (d / 256 roundings
+    counting each product and each add, generously), then a tree of 12 levels
+    (64 lanes, 16 waves) and the bias. With scratch: in a K part of Kp, each of 4
+    chains takes Kp / 16 MFMA steps of 4 products (at most 5 roundings a
+    step), the chains are added pairwise (2), each of 4 waves adds P / 4
+    parts, the waves pairwise (2), then the bias (1); P from the scratch size
+    moe_route asks for."""
+    P = mb.moe_route_workspace_bytes(dims) // (cfg.S * cfg.E * 4)
+    if P == 0:
+        return cfg.d / 256 + 12
+    return 5 * (cfg.d / P) / 16 + 2 + P / 4 + 2 + 1
+
+
 def check_logits(inp, g) -> np.ndarray:
     """GPU fp32 logits against the fp64 oracle; returns the oracle's logits."""
     cfg = inp["cfg"]
     lo = oracle.router_logits(inp["x"], inp["wr"], inp.get("bias") if cfg.bias_mode == 0 else None)
     mag = np.abs(bf16_val(inp["x"])) @ np.abs(inp["wr"].astype(np.float64)).T
     u = 2.0**-24
-    n = cfg.d / 256 + 12
+    n = logit_roundings(cfg, g["blk"].dims)
     tol = n * u * mag + u * np.abs(lo) + 1e-30
     err = np.abs(g["logits"].astype(np.float64) - lo)
     assert np.all(err <= tol), f"logit error {err.max():.3g} > bound {tol[np.argmax(err / tol)]:.3g}"
@@ -105,8 +124,11 @@ def check_bucket(inp, g) -> dict:
 
 def gpu_h(g, cfg) -> tuple[np.ndarray, np.ndarray | None]:
     """The SwiGLU rows the FFN left in its workspace: routed [R_max][I] and,
-    with a shared expert, [S][I_s]."""
+    with a shared expert, [S][I_s]. moe_forward's workspace holds moe_route's
+    scratch first, then the FFN's."""
     ws = to_np(g["blk"].fws if g.get("fused") else g["blk"].ws)
+    if g.get("fused"):
+        ws = ws[mb.moe_route_workspace_bytes(g["blk"].dims):]
     R = cfg.S * min(cfg.topk, cfg.n_local)
     nb = R * cfg.I * 2
     h = ws[:nb].view(np.uint16).reshape(R, cfg.I)

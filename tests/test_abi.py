@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert mb.moe_abi_version() == mb.ABI_VERSION == 2
+    assert mb.moe_abi_version() == mb.ABI_VERSION == 3
     for code in range(-6, 1):
         s = mb.moe_status_string(code)
         assert s and s != "unknown status"
@@ -107,16 +107,38 @@ def _rc(fn, *args):
 def test_route_rejects():
     d = ctypes.byref(dims())
     ok = [FAKE] * 6
-    assert _rc("moe_route", None, *ok, None) == mb.MOE_ERR_NULL
-    assert _rc("moe_route", ctypes.byref(dims(S=0)), *ok, None) == mb.MOE_ERR_SHAPE
+    assert _rc("moe_route", None, *ok, None, 0, None) == mb.MOE_ERR_NULL
+    assert _rc("moe_route", ctypes.byref(dims(S=0)), *ok, None, 0, None) == mb.MOE_ERR_SHAPE
     for i in (0, 1, 3, 4, 5):  # bias (2) may be NULL
         a = list(ok)
         a[i] = None
-        assert _rc("moe_route", d, *a, None) == mb.MOE_ERR_NULL, i
+        assert _rc("moe_route", d, *a, None, 0, None) == mb.MOE_ERR_NULL, i
     for i in range(6):
         a = list(ok)
         a[i] = MIS
-        assert _rc("moe_route", d, *a, None) == mb.MOE_ERR_ALIGN, i
+        assert _rc("moe_route", d, *a, None, 0, None) == mb.MOE_ERR_ALIGN, i
+
+
+def test_route_workspace():
+    """S <= 32 needs no scratch; beyond, the router's K parts [P, S, E] fp32
+    with P a power of two up to 32 that divides d / 16."""
+    assert mb.moe_route_workspace_bytes(dims(S=16)) == 0
+    assert mb.moe_route_workspace_bytes(dims(S=32)) == 0
+    assert mb.moe_route_workspace_bytes(dims(S=0)) == 0
+    for S, d, E in ((33, 256, 8), (64, 4096, 256), (128, 7168, 256), (33, 384, 32)):
+        n = mb.moe_route_workspace_bytes(dims(S=S, d=d, E=E, n_local=min(E, 8), topk=2))
+        P = n // (S * E * 4)
+        assert n == P * S * E * 4 or (n - P * S * E * 4) < 256
+        assert P >= 1 and P & (P - 1) == 0 and P <= 32 and (d // 16) % P == 0, (S, d, E, P)
+    wd = ctypes.byref(dims(S=64, d=4096, E=256, n_local=32, topk=8))
+    need = mb.moe_route_workspace_bytes(dims(S=64, d=4096, E=256, n_local=32, topk=8))
+    ok = [FAKE] * 6
+    assert _rc("moe_route", wd, *ok, None, need, None) == mb.MOE_ERR_NULL
+    assert _rc("moe_route", wd, *ok, MIS, need, None) == mb.MOE_ERR_ALIGN
+    assert _rc("moe_route", wd, *ok, FAKE, need - 1, None) == mb.MOE_ERR_WORKSPACE
+    # the forward workspace holds the router's scratch and the FFN's
+    fd = dims(S=64, d=4096, E=256, n_local=32, topk=8)
+    assert mb.moe_forward_workspace_bytes(fd) == need + mb.moe_ffn_workspace_bytes(fd)
 
 
 def test_bucket_rejects():
