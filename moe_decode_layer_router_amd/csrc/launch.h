@@ -22,13 +22,20 @@ inline const float* select_bias(const moe_dims& m, const float* bias) {
 // MI355X, us, whole-K workgroups against split tiles: S = 32 10.2 / 10.7,
 // S = 64 13.4 / 11.4, S = 96 18.7 / 14.9, S = 128 (d = 7168) 27.1 / 18.0.
 constexpr int kRouteSplitMinS = 32;
+#ifndef MOE_ROUTE_MAX_PARTS
+#define MOE_ROUTE_MAX_PARTS 32
+#endif
+#ifndef MOE_ROUTE_MAX_WG
+#define MOE_ROUTE_MAX_WG 256
+#endif
+constexpr int kMaxRouteParts = MOE_ROUTE_MAX_PARTS;  // K parts of the split router, at most
 inline int router_tile_tok(int S) { return S <= 64 ? 32 : 64; }
 inline int router_parts(const moe_dims& m) {
   if (m.S <= kRouteSplitMinS) return 0;
   const int TT = router_tile_tok(m.S);
   const int tiles = ((m.S + TT - 1) / TT) * ((m.E + 63) / 64);
   int P = 1;
-  while (P < 32 && tiles * P * 2 <= 256 && (m.d / 16) % (2 * P) == 0) P *= 2;  // <= kMaxRouteParts
+  while (P < kMaxRouteParts && tiles * P * 2 <= MOE_ROUTE_MAX_WG && (m.d / 16) % (2 * P) == 0) P *= 2;
   return P;
 }
 // scratch of the split router: parts [P][S][E] fp32

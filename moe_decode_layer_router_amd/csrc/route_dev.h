@@ -11,6 +11,7 @@
 #pragma once
 
 #include "common.h"
+#include "launch.h"
 
 namespace moeblk {
 
@@ -431,7 +432,6 @@ constexpr int kRouteTileE = 64;
 #define MOE_ROUTE_RING 8
 #endif
 constexpr int kRouteRing = MOE_ROUTE_RING;  // 16-K blocks in flight a wave
-constexpr int kMaxRouteParts = 32;          // K parts of the split router, at most
 
 template <int NT>
 struct RouteBlk {
