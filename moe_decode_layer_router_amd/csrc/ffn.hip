@@ -16,7 +16,7 @@
 //   boundary carries the dependency. Grid of each: the shared expert's tasks
 //   first, then the routed items, then workgroups past the last item.
 //
-// Work items hold 16 bucket rows for S <= 16, else 32.
+// Work items hold 16 bucket rows, or 32 with a shared expert at S > 16.
 //
 // The host does not know the bucket sizes, so a grid covers the largest
 // possible number of items.
@@ -72,45 +72,28 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
     __hip_atomic_store(&flags[i * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The single launch (no shared expert); TTG token tiles an item, PG / PD:
-// chunks in flight a wave in gate_up / down tasks. Forward progress: every
-// gate_up workgroup id is below every down workgroup id, and workgroups are
-// dispatched in id order, so when a down task waits, every gate_up task has
-// been dispatched; gate_up tasks wait for nothing. A wait is bounded (about a
-// second) and sets the error word if it ever hits the bound.
+// The single launch (no shared expert), items of 16 bucket rows at every S;
+// PG / PD: chunks in flight a wave in gate_up / down tasks. Forward progress:
+// every gate_up workgroup id is below every down workgroup id, and workgroups
+// are dispatched in id order, so when a down task waits, every gate_up task
+// has been dispatched; gate_up tasks wait for nothing. A wait is bounded
+// (about a second) and sets the error word if it ever hits the bound.
+//
+// 16-row items at S > 16 too: a popular expert's weights are then read once
+// per 16 picks rather than per 32, but the kernel holds 4 workgroups a CU
+// (116 VGPRs) instead of 3 (168 for 32-row tiles). Measured steps, us, 16-row
+// items against 32-row items (those with their rows staged in LDS): S = 32
+// 58.8 / 60.2, S = 64 Zipf 50.2 / 51.4, S = 96 87.5 / 88.2.
 #ifndef MOE_SINGLE_PD
 #define MOE_SINGLE_PD 2  // down chunks in flight a wave (issued before the wait)
 #endif
 #ifndef MOE_SINGLE_OCC
 #define MOE_SINGLE_OCC 4  // workgroups a CU
 #endif
-// workgroups a CU for the 32-row groups (more registers a wave)
-#ifndef MOE_SINGLE_OCC2
-#define MOE_SINGLE_OCC2 3
-#endif
-// 32-row items holding at most 16 bucket rows that fit in kBigLdsB bytes of
-// LDS stage them there (ffn_task_ldsb), with this many weight chunks in flight
-// a wave (gate_up / down), all issued before the row copy (a down task: before
-// it waits). The LDS of three workgroups a CU fits. Measured FFN us at S = 32
-// / 96: 4 chunks 44.2 / 66.3, 3 chunks 44.2 / 67.0, 5 chunks 45.4 / 67.4; the
-// row copy after the first chunk 44.7 / 67.2.
-constexpr int kBigLdsB = 49152;
-#ifndef MOE_BIG_LDSB_PG
-#define MOE_BIG_LDSB_PG 4
-#endif
-#ifndef MOE_BIG_LDSB_PD
-#define MOE_BIG_LDSB_PD 4
-#endif
-template <int TTG, int PG, int PD>
-__global__ __launch_bounds__(kSplit * kWave, TTG == 1 ? MOE_SINGLE_OCC : MOE_SINGLE_OCC2) void
-ffn_single_kernel(FfnArgs a) {
-  // LDS: the partial tiles of the reduction; with 32-row items also the B rows
-  // of a task that stages them (ffn_task_ldsb)
-  constexpr int kRedBytes = static_cast<int>(sizeof(f32x4_t)) * kSplit * TTG * 4 * kWave;
-  constexpr int kSmem =
-      TTG == 2 && ldsb_smem<kBigLdsB>() > kRedBytes ? ldsb_smem<kBigLdsB>() : kRedBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
-  auto red = reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(smem);
+template <int PG, int PD>
+__global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_kernel(FfnArgs a) {
+  constexpr int TTG = 1;
+  __shared__ f32x4_t red[kSplit][TTG][4][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
   const int n_work = count_work<TTG>(cnt);
@@ -121,20 +104,8 @@ ffn_single_kernel(FfnArgs a) {
   if (t < n_work * RB13) {
     const int wi = t / RB13, rb = t - wi * RB13;
     find_task<TTG>(cnt, wi, el, row0, ntok);
-    el = __builtin_amdgcn_readfirstlane(el);
-    row0 = __builtin_amdgcn_readfirstlane(row0);
-    ntok = __builtin_amdgcn_readfirstlane(ntok);
     const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB13 + rb) * NC13 * kMxTileBytes;
     const int32_t* rows = a.rows;
-    if constexpr (TTG == 2) {
-      if (ntok <= 16 && ntok * a.d * 2 <= kBigLdsB) {
-        ffn_task_ldsb<MOE_BIG_LDSB_PG, MOE_BIG_LDSB_PG, kBigLdsB, true, true>(
-            tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; },
-            NoWait{}, smem);
-        publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
-        return;
-      }
-    }
     ffn_task<true, TTG, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
                                         [rows](int r) { return rows[r]; }, NoWait{}, red);
     publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
@@ -144,30 +115,11 @@ ffn_single_kernel(FfnArgs a) {
   if (t >= n_work * RB2) return;
   const int wi = t / RB2, rb = t - wi * RB2;
   find_task<TTG>(cnt, wi, el, row0, ntok);
-  el = __builtin_amdgcn_readfirstlane(el);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
-  ntok = __builtin_amdgcn_readfirstlane(ntok);
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB2 + rb) * NC2 * kMxTileBytes;
-  if constexpr (TTG == 2) {
-    if (ntok <= 16 && ntok * a.I * 2 <= kBigLdsB) {
-      ffn_task_ldsb<MOE_BIG_LDSB_PD, MOE_BIG_LDSB_PD, kBigLdsB, false, true>(
-          tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d, [](int r) { return r; },
-          WaitFlag{&a.ready[t * kCtlStride], a.error}, smem);
-      return;
-    }
-  }
   ffn_task<true, TTG, PD, false, true>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d,
                                        [](int r) { return r; },
                                        WaitFlag{&a.ready[t * kCtlStride], a.error}, red);
 }
-
-// chunks in flight a wave in the single launch for 32-token groups
-#ifndef MOE_BIG_PG
-#define MOE_BIG_PG 2
-#endif
-#ifndef MOE_BIG_PD
-#define MOE_BIG_PD 2
-#endif
 
 // chunks in flight a wave of the routed tasks in the two launches for
 // 32-token groups (measured at S = 128 with the shared expert, FFN us:
@@ -342,17 +294,14 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   a.n_loc = m.n_local;
   a.R_max = r_max(m);
   a.max_work = l.max_work;
-  const bool big = ffn_group(m) > 16;
   if (single_launch(m)) {
     const int grid = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
-    if (big)
-      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_BIG_PG, MOE_BIG_PD>), dim3(grid), dim3(kSplit * kWave), 0,
-                         stream, a);
-    else
-      hipLaunchKernelGGL((ffn_single_kernel<1, 2, MOE_SINGLE_PD>), dim3(grid), dim3(kSplit * kWave), 0,
-                         stream, a);
-  } else {  // a shared expert
-    big ? launch_pair<2, MOE_PAIR_PG, MOE_PAIR_PD, true>(a, stream) : launch_pair<1, 2, 4, true>(a, stream);
+    hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD>), dim3(grid), dim3(kSplit * kWave), 0,
+                       stream, a);
+  } else if (ffn_group(m) > 16) {  // a shared expert, 32-row items
+    launch_pair<2, MOE_PAIR_PG, MOE_PAIR_PD, true>(a, stream);
+  } else {
+    launch_pair<1, 2, 4, true>(a, stream);
   }
   return launch_status();
 }

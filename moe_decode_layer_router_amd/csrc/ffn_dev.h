@@ -337,8 +337,9 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
 // (17 VGPRs a chunk instead of 33), so a wave keeps PW weight chunks in flight
 // at the register cost of about PW / 2 chunks of the ring with activations,
 // and the LDS reads wait on their own counter, not behind the weight loads.
-// Items of 32 rows at S > 16 often hold only a few picks: the task then runs
-// one token tile instead of two.
+// The routed items of the two launches with a shared expert (32 rows at
+// S > 16) often hold only a few picks: the task then runs one token tile
+// instead of two.
 // Columns past the task's rows read its last row (an LDS broadcast) and are
 // never stored. After the main loop the same LDS holds the partial tiles of
 // the wave-order reduction (task_epilogue).

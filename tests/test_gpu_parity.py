@@ -292,18 +292,16 @@ def test_fused_repeated_calls_agree():
 
 
 # Bucket sizes on both sides of the limits of the routed tasks that stage their
-# rows in LDS (at most 16 rows, and rows x K x 2 bytes at most 48 KiB in the
-# single launch for S > 16, 64 KiB in the two launches with a shared
-# expert): (config, seed, the largest bucket that stages its gate_up or down
-# rows). The seeds give buckets on both sides (checked below).
+# rows in LDS, in the two launches with a shared expert (at most 16 rows, and
+# rows x K x 2 bytes at most 64 KiB): (config, seed, the largest bucket whose
+# gate_up or down task stages its rows). The seeds give buckets on both sides
+# (checked below).
 LDSB = {
-    # single launch, gate_up K = 4096: 6 rows stage, 7 .. 16 do not
-    "single_gate_up_d4096": (_tiny(S=40, d=4096, I=256, E=16, n_local=8, topk=4), 2, 6),
-    # single launch, down K = 2048: 12 rows (exactly 48 KiB) stage, 13 and 17 do not
-    "single_down_I2048": (_tiny(S=24, d=256, I=2048, E=8, n_local=8, topk=4), 0, 12),
-    # two launches, gate_up K = 7168: 4 rows stage, 5 .. 7 do not
+    # gate_up K = 7168: 4 rows stage, 5 .. 7 do not
     "pair_gate_up_d7168": (_tiny(S=40, d=7168, I=256, E=16, n_local=8, topk=2, shared_I=128), 0, 4),
-    # two launches with 16-row items (S <= 16)
+    # down K = 2048: 16 rows (exactly 64 KiB) stage, 17 .. 21 do not
+    "pair_down_I2048": (_tiny(S=64, d=256, I=2048, E=8, n_local=8, topk=2, shared_I=128), 0, 16),
+    # 16-row items (S <= 16)
     "pair_S16_d7168": (_tiny(S=16, d=7168, I=256, E=8, n_local=8, topk=2, shared_I=128), 0, 4),
 }
 
