@@ -143,6 +143,13 @@ constexpr int kPairLdsB = 65536;
 #ifndef MOE_PAIR_LDSB_PD
 #define MOE_PAIR_LDSB_PD 4
 #endif
+// chunks in flight a wave of the routed tasks of 32-row items that hold at
+// most 16 rows but do not fit the LDS budget (one token tile, register ring;
+// at S = 128 with the shared expert items of 5 to 8 rows at d = 7168: FFN
+// 159.0 us against 161.8 us with two token tiles; 3 chunks 159.1 us)
+#ifndef MOE_PAIR_TT1_P
+#define MOE_PAIR_TT1_P 2
+#endif
 
 // LDS of the two launches: the partial tiles of the reduction, or the B rows
 // of a routed task that stages them
@@ -192,6 +199,12 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
         smem);
     return;
   }
+  if (TTG > 1 && ntok <= 16) {  // one token tile: half the MFMAs and activation loads
+    ffn_task<true, 1, MOE_PAIR_TT1_P, true, false>(
+        tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; }, NoWait{},
+        reinterpret_cast<f32x4_t(*)[1][4][kWave]>(smem));
+    return;
+  }
   ffn_task<true, TTG, P, true, false>(tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I,
                                       [rows](int r) { return rows[r]; }, NoWait{},
                                       reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
@@ -233,6 +246,12 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
   if (ntok <= 16 && ntok * a.I * 2 <= kPairLdsB) {
     ffn_task_ldsb<MOE_PAIR_LDSB_PD, 1, kPairLdsB, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb,
                                                             a.y, a.d, same, NoWait{}, smem);
+    return;
+  }
+  if (TTG > 1 && ntok <= 16) {
+    ffn_task<true, 1, MOE_PAIR_TT1_P, false, false>(
+        tiles, NC, a.h, a.I, row0, ntok, rb, a.y, a.d, same, NoWait{},
+        reinterpret_cast<f32x4_t(*)[1][4][kWave]>(smem));
     return;
   }
   ffn_task<true, TTG, P, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb, a.y, a.d, same,
