@@ -44,9 +44,9 @@ inline size_t router_parts_bytes(const moe_dims& m) {
 }
 
 // the router (applies logit_bias itself) and the top-k (select_bias). With
-// `parts` (router_parts_bytes of scratch) and S > 16 the router writes its K
-// parts there and the top-k sums them into `logits`; without, the router
-// writes `logits` itself.
+// `parts` (router_parts_bytes of scratch) and S > kRouteSplitMinS the router
+// writes its K parts there and the top-k sums them into `logits_out`;
+// otherwise the router writes `logits` itself.
 void launch_router_logits(const moe_dims& m, const void* x, const float* wr, const float* bias,
                           float* logits, hipStream_t stream, float* parts = nullptr);
 void launch_topk(const moe_dims& m, const float* logits, const float* bias, int32_t* ids, float* w,
