@@ -323,3 +323,35 @@ def test_lds_staged_task_limits(name):
     assert np.array_equal(g["y"][:n], gf["y"][:n])
     if cfg.shared_I:
         assert np.array_equal(g["y"][R:], gf["y"][R:])
+
+
+# The shared expert's 32-token groups at ragged S (33: a 1-token last group;
+# 100: a 4-token one), S = 32 (one group), S = 128 with d = 128 (one K chunk),
+# d = 1152 (an odd chunk count) and d = 7168; a second call on the same
+# workspace gives the same bits, and so does the one-call path.
+SG_GROUPS = {
+    "S33_d1152": _tiny(S=33, d=1152, I=128, E=8, n_local=4, topk=2, shared_I=256),
+    "S128_d128": _tiny(S=128, d=128, I=128, E=8, n_local=8, topk=2, shared_I=384),
+    "S100_d2048": _tiny(S=100, d=2048, I=256, E=16, n_local=4, topk=2, shared_I=128),
+    "S64_d7168": _tiny(S=64, d=7168, I=128, E=16, n_local=2, topk=1, shared_I=256),
+    "S32_d640": _tiny(S=32, d=640, I=128, E=8, n_local=4, topk=2, shared_I=128),
+}
+
+
+@pytest.mark.parametrize("name", list(SG_GROUPS))
+def test_shared_token_groups(name):
+    cfg = SG_GROUPS[name]
+    inp = make_inputs(cfg, 5, gamma="random")
+    g = run_gpu(inp)
+    check_block(inp, g, strict=False)
+    R = g["blk"].dims.r_max
+    # a second call on the same workspace
+    g["blk"].y.fill_(0)
+    g2 = run_gpu(inp, g["blk"])
+    assert np.array_equal(g["y"][R:], g2["y"][R:])
+    assert np.array_equal(g["out"], g2["out"])
+    # the one-call path: bit-identical
+    g["blk"].out.fill_(float("nan"))
+    gf = run_gpu(inp, g["blk"], fused=True)
+    assert np.array_equal(g["y"][R:], gf["y"][R:])
+    assert np.array_equal(g["out"], gf["out"])
