@@ -11,7 +11,9 @@
 //   itself in prod[item] once its stores are done; the last one of the item
 //   sets a ready flag for each of the item's down tasks. A down task issues
 //   its first weight loads, then waits for its flag, then reads the SwiGLU
-//   rows with coherent loads: its weights stream while gate_up finishes.
+//   rows with coherent loads: its weights stream while gate_up finishes. At
+//   S > 32 each wave also stages two more weight chunks in LDS before it
+//   waits.
 // * With a shared expert: two launches, gate_up + SwiGLU then down; the kernel
 //   boundary carries the dependency. Grid of each: the shared expert's tasks
 //   first, then the routed items, then workgroups past the last item.
@@ -90,10 +92,22 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
 #ifndef MOE_SINGLE_OCC
 #define MOE_SINGLE_OCC 4  // workgroups a CU
 #endif
-template <int PG, int PD>
+// PL: down chunks a wave staged in LDS before the wait (besides PD in
+// registers), 2 at S > 32 and none below. Measured FFN us without / with:
+// S = 8 22.15 / 22.50, S = 16 46.95 / 47.49, S = 32 40.97 / 41.43,
+// S = 64 (Zipf) 31.54 / 30.62, S = 96 64.12 / 62.79. The extra bytes in
+// flight pay once the tasks outnumber the resident workgroups; below that
+// they compete with the gate_up tasks' weight stream.
+#ifndef MOE_SINGLE_PL_LARGE_S
+#define MOE_SINGLE_PL_LARGE_S 2
+#endif
+template <int PG, int PD, int PL>
 __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_kernel(FfnArgs a) {
   constexpr int TTG = 1;
-  __shared__ f32x4_t red[kSplit][TTG][4][kWave];
+  constexpr int kRed = static_cast<int>(sizeof(f32x4_t)) * kSplit * TTG * 4 * kWave;
+  constexpr int kStage = kSplit * PL * kMxTileBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRed > kStage ? kRed : kStage];
+  auto red = reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(smem);
   const int lane = threadIdx.x & (kWave - 1);
   const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
   const int n_work = count_work<TTG>(cnt);
@@ -116,7 +130,7 @@ __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_ker
   const int wi = t / RB2, rb = t - wi * RB2;
   find_task<TTG>(cnt, wi, el, row0, ntok);
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB2 + rb) * NC2 * kMxTileBytes;
-  ffn_task<true, TTG, PD, false, true>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d,
+  ffn_task<true, TTG, PD, false, true, false, PL>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d,
                                        [](int r) { return r; },
                                        WaitFlag{&a.ready[t * kCtlStride], a.error}, red);
 }
@@ -315,8 +329,12 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   a.max_work = l.max_work;
   if (single_launch(m)) {
     const int grid = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
-    hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD>), dim3(grid), dim3(kSplit * kWave), 0,
-                       stream, a);
+    if (m.S > 32)
+      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, MOE_SINGLE_PL_LARGE_S>), dim3(grid),
+                         dim3(kSplit * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, 0>), dim3(grid), dim3(kSplit * kWave),
+                         0, stream, a);
   } else if (ffn_group(m) > 16) {  // a shared expert, 32-row items
     launch_pair<2, MOE_PAIR_PG, MOE_PAIR_PD, true>(a, stream);
   } else {

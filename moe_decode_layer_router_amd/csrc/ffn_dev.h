@@ -164,6 +164,34 @@ __device__ __forceinline__ void load_w(BfChunk<TTG>& ch, const uint8_t* wlane, c
       ch.w[r][q] = *reinterpret_cast<const u32x4_t*>(t + r * 4096 + q * 1024);
 }
 
+// One MXFP4 chunk tile (kMxTileBytes: 4 row tiles of 64 lanes x 16 bytes, then
+// 64 lanes x 4 scale bytes) of chunk c copied to LDS at dst by the wave, with
+// loads that write LDS directly (lane l's piece lands at dst + l x size).
+__device__ __forceinline__ void stage_mx_lds(uint8_t* dst, const uint8_t* tiles, int c) {
+  typedef const __attribute__((address_space(1))) void* gptr_t;
+  typedef __attribute__((address_space(3))) void* lptr_t;
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint8_t* src = tiles + static_cast<size_t>(c) * kMxTileBytes;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    __builtin_amdgcn_global_load_lds((gptr_t)(src + r * 1024 + lane * 16), (lptr_t)(dst + r * 1024),
+                                     16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gptr_t)(src + 4096 + lane * 4), (lptr_t)(dst + 4096), 4, 0, 0);
+}
+
+// The weights of an MXFP4 chunk from a tile staged by stage_mx_lds. The
+// compiler does not order LDS reads after these direct LDS loads, so the wave
+// first waits for all of its vector loads (the "memory" clobber keeps the
+// reads below the wait).
+template <int TTG>
+__device__ __forceinline__ void lds_mx_chunk(MxChunk<TTG>& ch, const uint8_t* src) {
+  const int lane = threadIdx.x & (kWave - 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ch.w[r] = *reinterpret_cast<const u32x4_t*>(src + r * 1024 + lane * 16);
+  ch.s = *reinterpret_cast<const uint32_t*>(src + 4096 + lane * 4);
+}
+
 template <int TTG>
 __device__ __forceinline__ void compute_chunk(const MxChunk<TTG>& ch, f32x4_t (&acc)[TTG][4],
                                               int n_tt) {
@@ -261,8 +289,13 @@ struct NoWait {
 // coherence point, down reads them from there). kF32Out (not gate_up): out
 // holds fp32 rows (a split-K partial), written unrounded through to the
 // coherence point, for another workgroup to sum.
-template <bool kMx, int TTG, int P, bool kGateUp, bool kCoh, bool kF32Out = false, class SrcOf,
-          class BeforeB>
+// PL > 0 (MXFP4 only): the wave's chunks P .. P + PL - 1 go to LDS (red, PL
+// chunk tiles a wave) before before_b(), by loads that write LDS directly, and
+// are read from there when the ring takes them: a task that waits (a down task
+// of the single launch) then has P + PL chunks in flight at the register cost
+// of P. The LDS is read only after every vector load of the wave has arrived.
+template <bool kMx, int TTG, int P, bool kGateUp, bool kCoh, bool kF32Out = false, int PL = 0,
+          class SrcOf, class BeforeB>
 __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int NC,
                                          const uint16_t* __restrict__ bsrc, int K, int row0,
                                          int ntok, int rb, uint16_t* __restrict__ out, int out_ld,
@@ -284,10 +317,28 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
   for (int tt = 0; tt < TTG; ++tt) src[tt] = src_of(row0 + min(tt * 16 + col, ntok - 1));
 
   using Chunk = typename std::conditional<kMx, MxChunk<TTG>, BfChunk<TTG>>::type;
+  static_assert(PL == 0 || kMx, "LDS-staged chunks are MXFP4 tiles");
   const int my_n = (NC - w + kSplit - 1) / kSplit;  // this wave's chunks: w, w + 4, ...
   Chunk ring[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) load_w<TTG>(ring[i], wlane, slane, min(w + kSplit * i, NC - 1));
+
+  uint8_t* lw = reinterpret_cast<uint8_t*>(red) + w * (PL * kMxTileBytes);  // this wave's LDS chunks
+  if constexpr (PL > 0) {
+#pragma unroll
+    for (int l = 0; l < PL; ++l)
+      if (P + l < my_n) stage_mx_lds(lw + l * kMxTileBytes, tiles, w + kSplit * (P + l));
+  }
+  // the ring takes the wave's chunk j (chunk w + 4 j)
+  auto refill = [&](Chunk& ch, int j) {
+    if constexpr (PL > 0) {
+      if (j < P + PL) {
+        lds_mx_chunk<TTG>(ch, lw + (j - P) * kMxTileBytes);
+        return;
+      }
+    }
+    load_w<TTG>(ch, wlane, slane, w + kSplit * j);
+  };
 
   before_b();
 
@@ -308,7 +359,7 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
     for (int i = 0; i < P; ++i) {
       compute_chunk<TTG>(ring[i], acc, n_tt);
       const int c = w + kSplit * (j0 + i + P);
-      load_w<TTG>(ring[i], wlane, slane, c);
+      refill(ring[i], j0 + i + P);
       bp.load(ring[i].b, c);
     }
   }
@@ -318,7 +369,7 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
       compute_chunk<TTG>(ring[i], acc, n_tt);
       if (j0 + i + P < my_n) {
         const int c = w + kSplit * (j0 + i + P);
-        load_w<TTG>(ring[i], wlane, slane, c);
+        refill(ring[i], j0 + i + P);
         bp.load(ring[i].b, c);
       }
     }
