@@ -14,9 +14,11 @@
 //   rows with coherent loads: its weights stream while gate_up finishes. At
 //   S > 32 each wave also stages two more weight chunks in LDS before it
 //   waits.
-// * With a shared expert: two launches, gate_up + SwiGLU then down; the kernel
-//   boundary carries the dependency. Grid of each: the shared expert's tasks
-//   first, then the routed items, then workgroups past the last item.
+// * With a shared expert: gate_up + SwiGLU, then down; the kernel boundary
+//   carries the dependency. Grid of each: the shared expert's tasks first,
+//   then the routed items, then workgroups past the last item. With 32-row
+//   items (S > 16) the down step is two launches, the routed tasks then the
+//   shared expert's.
 //
 // Work items hold 16 bucket rows, or 32 with a shared expert at S > 16.
 //
@@ -167,12 +169,26 @@ constexpr int kPairLdsB = 65536;
 
 // LDS of the two launches: the partial tiles of the reduction, or the B rows
 // of a routed task that stages them
-template <int TTG>
+template <int TTG, int kLdsB = kPairLdsB>
 constexpr int pair_smem() {
   constexpr int red = static_cast<int>(sizeof(f32x4_t)) * kSplit *
                       (kSharedTTG > TTG ? kSharedTTG : TTG) * 4 * kWave;
-  return red > ldsb_smem<kPairLdsB>() ? red : ldsb_smem<kPairLdsB>();
+  return red > ldsb_smem<kLdsB>() ? red : ldsb_smem<kLdsB>();
 }
+
+// With 32-row items (S > 16) the down step is two launches: the routed tasks
+// alone, then the shared expert's. Without the shared path's bf16 tiles (243
+// VGPRs) and with rows of at most MOE_DOWN_LDSB bytes staged in LDS, the routed
+// launch holds MOE_DOWN_OCC workgroups a CU instead of 2. Measured at S = 128
+// (d = 7168, I = 2048): routed 41.4 us + shared 15.8 us, against 60.6 us as
+// one launch; steps 184.4 / 184.8 against 187.2 / 187.5 us (3 workgroups a CU
+// with 48 KiB: 43.2 + 16.0 us, step 185.4 us).
+#ifndef MOE_DOWN_OCC
+#define MOE_DOWN_OCC 4
+#endif
+#ifndef MOE_DOWN_LDSB
+#define MOE_DOWN_LDSB 32768
+#endif
 
 template <int TTG, int P, bool kShared>
 __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
@@ -224,9 +240,12 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
                                       reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }
 
-template <int TTG, int P, bool kShared>
-__global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG>()];
+// kShared / kRouted: the launch runs the shared expert's tasks / the routed
+// tasks (in that order when both); OCC workgroups a CU; routed tasks with
+// rows of at most kLdsB bytes stage them in LDS.
+template <int TTG, int P, bool kShared, bool kRouted = true, int OCC = 2, int kLdsB = kPairLdsB>
+__global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG, kLdsB>()];
   auto red = reinterpret_cast<f32x4_t(*)[kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave]>(smem);
   const int RB = a.d / kRowsPerBlock;
   auto same = [](int r) { return r; };
@@ -247,6 +266,7 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
     }
     t -= n_sg * RB;
   }
+  if constexpr (!kRouted) return;
   const int NC = a.I / kChunkK;
   const int wi = t / RB, rb = t - wi * RB;
   const int lane = threadIdx.x & (kWave - 1);
@@ -257,8 +277,8 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
   row0 = __builtin_amdgcn_readfirstlane(row0);
   ntok = __builtin_amdgcn_readfirstlane(ntok);
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
-  if (ntok <= 16 && ntok * a.I * 2 <= kPairLdsB) {
-    ffn_task_ldsb<MOE_PAIR_LDSB_PD, 1, kPairLdsB, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb,
+  if (ntok <= 16 && ntok * a.I * 2 <= kLdsB) {
+    ffn_task_ldsb<MOE_PAIR_LDSB_PD, 1, kLdsB, false, false>(tiles, NC, a.h, a.I, row0, ntok, rb,
                                                             a.y, a.d, same, NoWait{}, smem);
     return;
   }
@@ -272,16 +292,25 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void down_kernel(FfnArgs a) {
                                        NoWait{}, reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }
 
-// PG / PD: chunks in flight a wave in gate_up / down
-template <int TTG, int PG, int PD, bool kShared>
+// PG / PD: chunks in flight a wave in gate_up / down; kSplitDown: the routed
+// and the shared down tasks in two launches
+template <int TTG, int PG, int PD, bool kShared, bool kSplitDown>
 void launch_pair(const FfnArgs& a, hipStream_t stream) {
   constexpr int GS = 16 * kSharedTTG;
   const int n_sg = kShared ? (a.S + GS - 1) / GS : 0;
+  const int RB2 = a.d / kRowsPerBlock;
   const int g1 = n_sg * (2 * a.Is / kRowsPerBlock) + a.max_work * (2 * a.I / kRowsPerBlock);
-  const int g2 = (n_sg + a.max_work) * (a.d / kRowsPerBlock);
   hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared>), dim3(g1), dim3(kSplit * kWave), 0, stream,
                      a);
-  hipLaunchKernelGGL((down_kernel<TTG, PD, kShared>), dim3(g2), dim3(kSplit * kWave), 0, stream, a);
+  if constexpr (kSplitDown && kShared) {
+    hipLaunchKernelGGL((down_kernel<TTG, PD, false, true, MOE_DOWN_OCC, MOE_DOWN_LDSB>),
+                       dim3(a.max_work * RB2), dim3(kSplit * kWave), 0, stream, a);
+    hipLaunchKernelGGL((down_kernel<TTG, PD, true, false>), dim3(n_sg * RB2), dim3(kSplit * kWave),
+                       0, stream, a);
+  } else {
+    hipLaunchKernelGGL((down_kernel<TTG, PD, kShared>), dim3((n_sg + a.max_work) * RB2),
+                       dim3(kSplit * kWave), 0, stream, a);
+  }
 }
 
 bool single_launch(const moe_dims& m) { return m.shared_I == 0; }
@@ -336,9 +365,9 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
       hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, 0>), dim3(grid), dim3(kSplit * kWave),
                          0, stream, a);
   } else if (ffn_group(m) > 16) {  // a shared expert, 32-row items
-    launch_pair<2, MOE_PAIR_PG, MOE_PAIR_PD, true>(a, stream);
-  } else {
-    launch_pair<1, 2, 4, true>(a, stream);
+    launch_pair<2, MOE_PAIR_PG, MOE_PAIR_PD, true, true>(a, stream);
+  } else {  // one down launch: the routed-only one would spill at 16-row items
+    launch_pair<1, 2, 4, true, false>(a, stream);
   }
   return launch_status();
 }
