@@ -17,8 +17,8 @@
 // * With a shared expert: gate_up + SwiGLU, then down; the kernel boundary
 //   carries the dependency. Grid of each: the shared expert's tasks first,
 //   then the routed items, then workgroups past the last item. With 32-row
-//   items (S > 16) the down step is two launches, the routed tasks then the
-//   shared expert's.
+//   items (S > 16) the shared expert's down tasks give each wave a row tile
+//   (shared_down_task), which lets the down launch hold 4 workgroups a CU.
 //
 // Work items hold 16 bucket rows, or 32 with a shared expert at S > 16.
 //
@@ -176,13 +176,15 @@ constexpr int pair_smem() {
   return red > ldsb_smem<kLdsB>() ? red : ldsb_smem<kLdsB>();
 }
 
-// With 32-row items (S > 16) the down step is two launches: the routed tasks
-// alone, then the shared expert's. Without the shared path's bf16 tiles (243
-// VGPRs) and with rows of at most MOE_DOWN_LDSB bytes staged in LDS, the routed
-// launch holds MOE_DOWN_OCC workgroups a CU instead of 2. Measured at S = 128
-// (d = 7168, I = 2048): routed 41.4 us + shared 15.8 us, against 60.6 us as
-// one launch; steps 184.4 / 184.8 against 187.2 / 187.5 us (3 workgroups a CU
-// with 48 KiB: 43.2 + 16.0 us, step 185.4 us).
+// With 32-row items (S > 16) the down launch runs the shared expert's tasks as
+// shared_down_task (waves own row tiles, the group's rows staged in LDS: 128
+// VGPRs instead of the bf16 ring's 243) and stages routed rows of at most
+// MOE_DOWN_LDSB bytes in LDS, so it holds MOE_DOWN_OCC workgroups a CU
+// instead of 2. Measured at S = 128 (d = 7168, I = 2048), down step: 49.1 us,
+// against 60.6 us as one launch at 2 workgroups a CU and 41.0 + 15.7 us as
+// two launches (routed tasks alone at 4 a CU, then the old shared tasks);
+// steps 176.3 / 177.0 against 184.5 / 185.3 us for the two launches. A ring of
+// 2 chunks in the shared task: 49.9 us.
 #ifndef MOE_DOWN_OCC
 #define MOE_DOWN_OCC 4
 #endif
@@ -240,12 +242,16 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
                                       reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }
 
-// kShared / kRouted: the launch runs the shared expert's tasks / the routed
-// tasks (in that order when both); OCC workgroups a CU; routed tasks with
-// rows of at most kLdsB bytes stage them in LDS.
-template <int TTG, int P, bool kShared, bool kRouted = true, int OCC = 2, int kLdsB = kPairLdsB>
+// Grid: the shared expert's tasks (kShared), then the routed items. OCC
+// workgroups a CU; routed tasks with rows of at most kLdsB bytes stage them in
+// LDS; kSgRows: the shared tasks run as shared_down_task.
+#ifndef MOE_SD_PW
+#define MOE_SD_PW 4  // weight chunks in flight a wave, shared_down_task
+#endif
+template <int TTG, int P, bool kShared, int OCC = 2, int kLdsB = kPairLdsB, bool kSgRows = false>
 __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG, kLdsB>()];
+  static_assert(!kSgRows || pair_smem<TTG, kLdsB>() >= kSdSmem, "LDS of the shared down task");
   auto red = reinterpret_cast<f32x4_t(*)[kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave]>(smem);
   const int RB = a.d / kRowsPerBlock;
   auto same = [](int r) { return r; };
@@ -259,14 +265,19 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
       group_task(t, n_sg, RB, rb, grp);
       const int row0 = grp * GS, ntok = min(GS, a.S - row0);
       const uint8_t* tiles = a.ws2 + static_cast<size_t>(rb) * NCs * kBfTileBytes;
-      ffn_task<false, kSharedTTG, kSharedP, false, false>(
-          tiles, NCs, a.hs, a.Is, row0, ntok, rb, a.y + static_cast<size_t>(a.R_max) * a.d, a.d,
-          same, NoWait{}, reinterpret_cast<f32x4_t(*)[kSharedTTG][4][kWave]>(&red[0][0][0][0]));
+      uint16_t* ys = a.y + static_cast<size_t>(a.R_max) * a.d;
+      if constexpr (kSgRows) {
+        static_assert(GS == kSdTok, "token groups of the shared down task");
+        shared_down_task<MOE_SD_PW>(tiles, NCs, a.hs, a.Is, row0, ntok, rb, ys, a.d, smem);
+      } else {
+        ffn_task<false, kSharedTTG, kSharedP, false, false>(
+            tiles, NCs, a.hs, a.Is, row0, ntok, rb, ys, a.d, same, NoWait{},
+            reinterpret_cast<f32x4_t(*)[kSharedTTG][4][kWave]>(&red[0][0][0][0]));
+      }
       return;
     }
     t -= n_sg * RB;
   }
-  if constexpr (!kRouted) return;
   const int NC = a.I / kChunkK;
   const int wi = t / RB, rb = t - wi * RB;
   const int lane = threadIdx.x & (kWave - 1);
@@ -292,25 +303,22 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
                                        NoWait{}, reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }
 
-// PG / PD: chunks in flight a wave in gate_up / down; kSplitDown: the routed
-// and the shared down tasks in two launches
-template <int TTG, int PG, int PD, bool kShared, bool kSplitDown>
+// PG / PD: chunks in flight a wave in gate_up / down; kLeanDown: the down
+// launch with shared_down_task at MOE_DOWN_OCC workgroups a CU
+template <int TTG, int PG, int PD, bool kShared, bool kLeanDown>
 void launch_pair(const FfnArgs& a, hipStream_t stream) {
   constexpr int GS = 16 * kSharedTTG;
   const int n_sg = kShared ? (a.S + GS - 1) / GS : 0;
-  const int RB2 = a.d / kRowsPerBlock;
   const int g1 = n_sg * (2 * a.Is / kRowsPerBlock) + a.max_work * (2 * a.I / kRowsPerBlock);
+  const int g2 = (n_sg + a.max_work) * (a.d / kRowsPerBlock);
   hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared>), dim3(g1), dim3(kSplit * kWave), 0, stream,
                      a);
-  if constexpr (kSplitDown && kShared) {
-    hipLaunchKernelGGL((down_kernel<TTG, PD, false, true, MOE_DOWN_OCC, MOE_DOWN_LDSB>),
-                       dim3(a.max_work * RB2), dim3(kSplit * kWave), 0, stream, a);
-    hipLaunchKernelGGL((down_kernel<TTG, PD, true, false>), dim3(n_sg * RB2), dim3(kSplit * kWave),
-                       0, stream, a);
-  } else {
-    hipLaunchKernelGGL((down_kernel<TTG, PD, kShared>), dim3((n_sg + a.max_work) * RB2),
+  if constexpr (kLeanDown)
+    hipLaunchKernelGGL((down_kernel<TTG, PD, kShared, MOE_DOWN_OCC, MOE_DOWN_LDSB, true>), dim3(g2),
                        dim3(kSplit * kWave), 0, stream, a);
-  }
+  else
+    hipLaunchKernelGGL((down_kernel<TTG, PD, kShared>), dim3(g2), dim3(kSplit * kWave), 0, stream,
+                       a);
 }
 
 bool single_launch(const moe_dims& m) { return m.shared_I == 0; }
@@ -366,7 +374,7 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
                          0, stream, a);
   } else if (ffn_group(m) > 16) {  // a shared expert, 32-row items
     launch_pair<2, MOE_PAIR_PG, MOE_PAIR_PD, true, true>(a, stream);
-  } else {  // one down launch: the routed-only one would spill at 16-row items
+  } else {  // 16-row items: at MOE_DOWN_OCC a CU their ring of 4 chunks would spill
     launch_pair<1, 2, 4, true, false>(a, stream);
   }
   return launch_status();

@@ -529,4 +529,114 @@ __device__ __forceinline__ void ffn_task_ldsb(const uint8_t* __restrict__ tiles,
                                          reinterpret_cast<f32x4_t(*)[1][4][kWave]>(smem));
 }
 
+// ---------------------------------------------------------------------------
+// The shared expert's down for one 64-row block and one group of up to 32
+// tokens (Kimi-K3 layer page, "k2_launch": w_sd, the always-on expert's down
+// projection), with waves owning row tiles instead of K quarters: wave w
+// streams row tile w over all NC chunks through a ring of PW chunks (16 VGPRs
+// a chunk) and needs no reduction across waves. The chunk's token rows (32 x
+// 128 bf16) are staged in LDS once for the 4 waves, two chunks ahead through
+// registers, in two buffers whose rows are padded to 272 bytes so that the 16
+// rows one ds_read_b128 touches fall on distinct banks. Workgroup-level;
+// smem: kSdSmem bytes. Output: bf16 rows row0 .. row0 + ntok - 1 of out.
+constexpr int kSdTok = 32;
+constexpr int kSdPitch = 136;                  // bf16 a staged row (128 + 8 pad)
+constexpr int kSdBuf = kSdTok * kSdPitch;      // bf16 a buffer
+constexpr int kSdSmem = 2 * kSdBuf * 2;        // bytes
+
+template <int PW>
+__device__ __forceinline__ void shared_down_task(const uint8_t* __restrict__ tiles, int NC,
+                                                 const uint16_t* __restrict__ hs, int Is, int row0,
+                                                 int ntok, int rb, uint16_t* __restrict__ out,
+                                                 int d, uint8_t* smem) {
+  static_assert(PW % 2 == 0, "the stage registers alternate with the chunk's parity");
+  constexpr int kThreads = kSplit * kWave;
+  constexpr int kPer = kSdTok * 16 / kThreads;  // 16-byte pieces a thread stages a chunk
+  constexpr int NTT = kSdTok / 16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int ntt = (ntok + 15) / 16;
+  uint16_t* lx = reinterpret_cast<uint16_t*>(smem);
+
+  // weights: row tile w of chunk c at tiles + c kBfTileBytes + w 4096 + q 1024
+  const uint8_t* wl = tiles + w * 4096 + lane * 16;
+  u32x4_t ring[PW][4];
+  auto load_wc = [&](u32x4_t (&r)[4], int c) {
+    const uint8_t* t = wl + static_cast<size_t>(c) * kBfTileBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const u32x4_t*>(t + q * 1024);
+  };
+  // token rows of chunk c: piece i * kThreads + tid = (token, 16-byte piece);
+  // tokens past the group's repeat its last row and are never stored
+  u32x4_t xs[2][kPer];
+  auto load_x = [&](u32x4_t (&v)[kPer], int c) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = i * kThreads + threadIdx.x;
+      const int t = row0 + min(q >> 4, ntok - 1);
+      v[i] = *reinterpret_cast<const u32x4_t*>(hs + static_cast<size_t>(t) * Is + c * kChunkK +
+                                               8 * (q & 15));
+    }
+  };
+  auto store_x = [&](const u32x4_t (&v)[kPer], int buf) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = i * kThreads + threadIdx.x;
+      *reinterpret_cast<u32x4_t*>(lx + buf * kSdBuf + (q >> 4) * kSdPitch + 8 * (q & 15)) = v[i];
+    }
+  };
+
+  f32x4_t acc[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  load_x(xs[0], 0);
+#pragma unroll
+  for (int i = 0; i < PW; ++i) load_wc(ring[i], min(i, NC - 1));
+  load_x(xs[1], min(1, NC - 1));
+  store_x(xs[0], 0);
+  if (NC > 2) load_x(xs[0], 2);
+
+  // chunk c: ring slot c % PW, staged rows in buffer c % 2; the stage
+  // registers xs[(c + 1) % 2] hold chunk c + 1, then receive chunk c + 3
+  for (int cb = 0; cb < NC; cb += PW) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int c = cb + i;
+      if (c < NC) {
+        __syncthreads();  // buffer c % 2 holds chunk c; buffer (c + 1) % 2 is free
+        const uint16_t* lb = lx + (c & 1) * kSdBuf + col * kSdPitch + 32 * g;
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+          if (tt < ntt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4_t b = *reinterpret_cast<const u32x4_t*>(lb + tt * 16 * kSdPitch + 8 * q);
+              acc[tt] = mfma_bf16(__builtin_bit_cast(bf16x8_t, ring[i][q]),
+                                  __builtin_bit_cast(bf16x8_t, b), acc[tt]);
+            }
+          }
+        }
+        if (c + PW < NC) load_wc(ring[i], c + PW);
+        if (c + 1 < NC) {
+          store_x(xs[(i + 1) & 1], (c + 1) & 1);  // PW is even: c + 1 and i + 1 agree mod 2
+          if (c + 3 < NC) load_x(xs[(i + 1) & 1], c + 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // rows 4g .. 4g + 3 of row tile w, token tt * 16 + col
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int c = tt * 16 + col;
+    if (tt >= ntt || c >= ntok) continue;
+    const int n0 = kRowsPerBlock * rb + 16 * w + 4 * g;
+    *reinterpret_cast<u32x2_t*>(out + static_cast<size_t>(row0 + c) * d + n0) =
+        u32x2_t{pack_bf16x2(acc[tt][0], acc[tt][1]), pack_bf16x2(acc[tt][2], acc[tt][3])};
+  }
+}
+
 }  // namespace moeblk
