@@ -17,8 +17,9 @@
 // * With a shared expert: gate_up + SwiGLU, then down; the kernel boundary
 //   carries the dependency. Grid of each: the shared expert's tasks first,
 //   then the routed items, then workgroups past the last item. With 32-row
-//   items (S > 16) the shared expert's down tasks give each wave a row tile
-//   (shared_down_task), which lets the down launch hold 4 workgroups a CU.
+//   items (S > 16) the shared expert's tasks give each wave a row tile
+//   (shared_rows_task), which lets the launches hold 3 (gate_up) and 4 (down)
+//   workgroups a CU.
 //
 // Work items hold 16 bucket rows, or 32 with a shared expert at S > 16.
 //
@@ -177,7 +178,7 @@ constexpr int pair_smem() {
 }
 
 // With 32-row items (S > 16) the down launch runs the shared expert's tasks as
-// shared_down_task (waves own row tiles, the group's rows staged in LDS: 128
+// shared_rows_task (waves own row tiles, the group's rows staged in LDS: 128
 // VGPRs instead of the bf16 ring's 243) and stages routed rows of at most
 // MOE_DOWN_LDSB bytes in LDS, so it holds MOE_DOWN_OCC workgroups a CU
 // instead of 2. Measured at S = 128 (d = 7168, I = 2048), down step: 49.1 us,
@@ -185,6 +186,18 @@ constexpr int pair_smem() {
 // two launches (routed tasks alone at 4 a CU, then the old shared tasks);
 // steps 176.3 / 177.0 against 184.5 / 185.3 us for the two launches. A ring of
 // 2 chunks in the shared task: 49.9 us.
+// The gate_up launch at S > 16 likewise runs the shared tasks as
+// shared_rows_task (154 VGPRs instead of 243) and stages routed rows of at
+// most MOE_GU_LDSB bytes (3 rows at d = 7168) at MOE_GU_OCC workgroups a CU.
+// Measured at S = 128, gate_up launch: 94.9 us against 101.1 us (bf16 ring,
+// 64 KiB, 2 a CU); 95.9 us at 4 a CU with 32 KiB, 103.6 us at 2 a CU with
+// 64 KiB; steps 170.8 / 171.6 against 177.1 / 177.1 us.
+#ifndef MOE_GU_OCC
+#define MOE_GU_OCC 3
+#endif
+#ifndef MOE_GU_LDSB
+#define MOE_GU_LDSB 49152
+#endif
 #ifndef MOE_DOWN_OCC
 #define MOE_DOWN_OCC 4
 #endif
@@ -192,9 +205,13 @@ constexpr int pair_smem() {
 #define MOE_DOWN_LDSB 32768
 #endif
 
-template <int TTG, int P, bool kShared>
-__global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG>()];
+#ifndef MOE_SG_PW
+#define MOE_SG_PW 4  // weight chunks in flight a wave, shared gate_up tasks
+#endif
+template <int TTG, int P, bool kShared, int OCC = 2, int kLdsB = kPairLdsB, bool kSgRows = false>
+__global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG, kLdsB>()];
+  static_assert(!kSgRows || pair_smem<TTG, kLdsB>() >= kSdSmem, "LDS of the shared task");
   auto red = reinterpret_cast<f32x4_t(*)[kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave]>(smem);
   const int NC = a.d / kChunkK;
   int t = blockIdx.x;
@@ -207,9 +224,14 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
       group_task(t, n_sg, RBs, rb, grp);
       const int row0 = grp * GS, ntok = min(GS, a.S - row0);
       const uint8_t* tiles = a.ws13 + static_cast<size_t>(rb) * NC * kBfTileBytes;
-      ffn_task<false, kSharedTTG, kSharedP, true, false>(
-          tiles, NC, a.x, a.d, row0, ntok, rb, a.hs, a.Is, [](int r) { return r; }, NoWait{},
-          reinterpret_cast<f32x4_t(*)[kSharedTTG][4][kWave]>(&red[0][0][0][0]));
+      if constexpr (kSgRows) {
+        static_assert(GS == kSdTok, "token groups of the shared task");
+        shared_rows_task<MOE_SG_PW, true>(tiles, NC, a.x, a.d, row0, ntok, rb, a.hs, a.Is, smem);
+      } else {
+        ffn_task<false, kSharedTTG, kSharedP, true, false>(
+            tiles, NC, a.x, a.d, row0, ntok, rb, a.hs, a.Is, [](int r) { return r; }, NoWait{},
+            reinterpret_cast<f32x4_t(*)[kSharedTTG][4][kWave]>(&red[0][0][0][0]));
+      }
       return;
     }
     t -= n_sg * RBs;
@@ -225,8 +247,8 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
   ntok = __builtin_amdgcn_readfirstlane(ntok);
   const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
   const int32_t* rows = a.rows;
-  if (ntok <= 16 && ntok * a.d * 2 <= kPairLdsB) {
-    ffn_task_ldsb<MOE_PAIR_LDSB_PG, 1, kPairLdsB, true, false>(
+  if (ntok <= 16 && ntok * a.d * 2 <= kLdsB) {
+    ffn_task_ldsb<MOE_PAIR_LDSB_PG, 1, kLdsB, true, false>(
         tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; }, NoWait{},
         smem);
     return;
@@ -244,9 +266,9 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void gate_up_kernel(FfnArgs a) {
 
 // Grid: the shared expert's tasks (kShared), then the routed items. OCC
 // workgroups a CU; routed tasks with rows of at most kLdsB bytes stage them in
-// LDS; kSgRows: the shared tasks run as shared_down_task.
+// LDS; kSgRows: the shared tasks run as shared_rows_task.
 #ifndef MOE_SD_PW
-#define MOE_SD_PW 4  // weight chunks in flight a wave, shared_down_task
+#define MOE_SD_PW 4  // weight chunks in flight a wave, shared down tasks
 #endif
 template <int TTG, int P, bool kShared, int OCC = 2, int kLdsB = kPairLdsB, bool kSgRows = false>
 __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
@@ -268,7 +290,7 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
       uint16_t* ys = a.y + static_cast<size_t>(a.R_max) * a.d;
       if constexpr (kSgRows) {
         static_assert(GS == kSdTok, "token groups of the shared down task");
-        shared_down_task<MOE_SD_PW>(tiles, NCs, a.hs, a.Is, row0, ntok, rb, ys, a.d, smem);
+        shared_rows_task<MOE_SD_PW, false>(tiles, NCs, a.hs, a.Is, row0, ntok, rb, ys, a.d, smem);
       } else {
         ffn_task<false, kSharedTTG, kSharedP, false, false>(
             tiles, NCs, a.hs, a.Is, row0, ntok, rb, ys, a.d, same, NoWait{},
@@ -303,17 +325,21 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
                                        NoWait{}, reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }
 
-// PG / PD: chunks in flight a wave in gate_up / down; kLeanDown: the down
-// launch with shared_down_task at MOE_DOWN_OCC workgroups a CU
-template <int TTG, int PG, int PD, bool kShared, bool kLeanDown>
+// PG / PD: chunks in flight a wave in gate_up / down; kLean: the shared tasks
+// as shared_rows_task, the launches at MOE_GU_OCC / MOE_DOWN_OCC workgroups a CU
+template <int TTG, int PG, int PD, bool kShared, bool kLean>
 void launch_pair(const FfnArgs& a, hipStream_t stream) {
   constexpr int GS = 16 * kSharedTTG;
   const int n_sg = kShared ? (a.S + GS - 1) / GS : 0;
   const int g1 = n_sg * (2 * a.Is / kRowsPerBlock) + a.max_work * (2 * a.I / kRowsPerBlock);
   const int g2 = (n_sg + a.max_work) * (a.d / kRowsPerBlock);
-  hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared>), dim3(g1), dim3(kSplit * kWave), 0, stream,
-                     a);
-  if constexpr (kLeanDown)
+  if constexpr (kLean)
+    hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared, MOE_GU_OCC, MOE_GU_LDSB, true>), dim3(g1),
+                       dim3(kSplit * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared>), dim3(g1), dim3(kSplit * kWave), 0,
+                       stream, a);
+  if constexpr (kLean)
     hipLaunchKernelGGL((down_kernel<TTG, PD, kShared, MOE_DOWN_OCC, MOE_DOWN_LDSB, true>), dim3(g2),
                        dim3(kSplit * kWave), 0, stream, a);
   else

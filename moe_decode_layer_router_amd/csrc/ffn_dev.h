@@ -530,25 +530,27 @@ __device__ __forceinline__ void ffn_task_ldsb(const uint8_t* __restrict__ tiles,
 }
 
 // ---------------------------------------------------------------------------
-// The shared expert's down for one 64-row block and one group of up to 32
-// tokens (Kimi-K3 layer page, "k2_launch": w_sd, the always-on expert's down
-// projection), with waves owning row tiles instead of K quarters: wave w
+// The shared expert for one 64-row block and one group of up to 32 tokens
+// (Kimi-K3 layer page, "k2_launch": w_sgu and w_sd, the always-on expert's
+// gate_up and down), with waves owning row tiles instead of K quarters: wave w
 // streams row tile w over all NC chunks through a ring of PW chunks (16 VGPRs
-// a chunk) and needs no reduction across waves. The chunk's token rows (32 x
-// 128 bf16) are staged in LDS once for the 4 waves, two chunks ahead through
-// registers, in two buffers whose rows are padded to 272 bytes so that the 16
-// rows one ds_read_b128 touches fall on distinct banks. Workgroup-level;
-// smem: kSdSmem bytes. Output: bf16 rows row0 .. row0 + ntok - 1 of out.
+// a chunk) and needs no reduction across waves. The chunk's B rows (32 x 128
+// bf16: token rows of x for gate_up, SwiGLU rows for down) are staged in LDS
+// once for the 4 waves, two chunks ahead through registers, in two buffers
+// whose rows are padded to 272 bytes so that the 16 rows one ds_read_b128
+// touches fall on distinct banks. Workgroup-level; smem: kSdSmem bytes.
+// Output rows row0 .. row0 + ntok - 1 of out (row length out_ld): gate_up
+// rounds gate and up to bf16 and writes SwiGLU rows, down writes bf16 rows.
 constexpr int kSdTok = 32;
 constexpr int kSdPitch = 136;                  // bf16 a staged row (128 + 8 pad)
 constexpr int kSdBuf = kSdTok * kSdPitch;      // bf16 a buffer
 constexpr int kSdSmem = 2 * kSdBuf * 2;        // bytes
 
-template <int PW>
-__device__ __forceinline__ void shared_down_task(const uint8_t* __restrict__ tiles, int NC,
-                                                 const uint16_t* __restrict__ hs, int Is, int row0,
+template <int PW, bool kGateUp>
+__device__ __forceinline__ void shared_rows_task(const uint8_t* __restrict__ tiles, int NC,
+                                                 const uint16_t* __restrict__ bsrc, int K, int row0,
                                                  int ntok, int rb, uint16_t* __restrict__ out,
-                                                 int d, uint8_t* smem) {
+                                                 int out_ld, uint8_t* smem) {
   static_assert(PW % 2 == 0, "the stage registers alternate with the chunk's parity");
   constexpr int kThreads = kSplit * kWave;
   constexpr int kPer = kSdTok * 16 / kThreads;  // 16-byte pieces a thread stages a chunk
@@ -575,7 +577,7 @@ __device__ __forceinline__ void shared_down_task(const uint8_t* __restrict__ til
     for (int i = 0; i < kPer; ++i) {
       const int q = i * kThreads + threadIdx.x;
       const int t = row0 + min(q >> 4, ntok - 1);
-      v[i] = *reinterpret_cast<const u32x4_t*>(hs + static_cast<size_t>(t) * Is + c * kChunkK +
+      v[i] = *reinterpret_cast<const u32x4_t*>(bsrc + static_cast<size_t>(t) * K + c * kChunkK +
                                                8 * (q & 15));
     }
   };
@@ -633,9 +635,17 @@ __device__ __forceinline__ void shared_down_task(const uint8_t* __restrict__ til
   for (int tt = 0; tt < NTT; ++tt) {
     const int c = tt * 16 + col;
     if (tt >= ntt || c >= ntok) continue;
-    const int n0 = kRowsPerBlock * rb + 16 * w + 4 * g;
-    *reinterpret_cast<u32x2_t*>(out + static_cast<size_t>(row0 + c) * d + n0) =
-        u32x2_t{pack_bf16x2(acc[tt][0], acc[tt][1]), pack_bf16x2(acc[tt][2], acc[tt][3])};
+    uint16_t* orow = out + static_cast<size_t>(row0 + c) * out_ld;
+    const f32x4_t v = acc[tt];
+    if constexpr (kGateUp) {  // gate i, gate i + 1, up i, up i + 1
+      const float g0 = round_bf16(v[0]), g1 = round_bf16(v[1]);
+      const float u0 = round_bf16(v[2]), u1 = round_bf16(v[3]);
+      *reinterpret_cast<uint32_t*>(orow + 32 * rb + 8 * w + 2 * g) =
+          swiglu_bf16_bits(g0, u0) | (swiglu_bf16_bits(g1, u1) << 16);
+    } else {
+      *reinterpret_cast<u32x2_t*>(orow + kRowsPerBlock * rb + 16 * w + 4 * g) =
+          u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
   }
 }
 

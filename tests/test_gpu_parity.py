@@ -293,12 +293,12 @@ def test_fused_repeated_calls_agree():
 
 # Bucket sizes on both sides of the limits of the routed tasks that stage their
 # rows in LDS, in the launches with a shared expert (at most 16 rows, and
-# rows x K x 2 bytes at most 64 KiB; 32 KiB in the down launch at S > 16),
-# and of the one-token-tile tasks (at most 16 rows): (config, seed,
+# rows x K x 2 bytes at most 64 KiB; at S > 16 48 KiB in gate_up and 32 KiB in
+# down), and of the one-token-tile tasks (at most 16 rows): (config, seed,
 # the limit). The seeds give buckets on both sides (checked below).
 LDSB = {
-    # gate_up K = 7168: 4 rows stage, 5 .. 7 do not
-    "pair_gate_up_d7168": (_tiny(S=40, d=7168, I=256, E=16, n_local=8, topk=2, shared_I=128), 0, 4),
+    # gate_up K = 7168 at S > 16: 3 rows stage, 4 .. 7 do not
+    "pair_gate_up_d7168": (_tiny(S=40, d=7168, I=256, E=16, n_local=8, topk=2, shared_I=128), 0, 3),
     # down K = 2048 at S > 16: 8 rows (exactly 32 KiB) stage, 9 .. 13 do not
     "pair_down_I2048_lds": (_tiny(S=36, d=256, I=2048, E=8, n_local=8, topk=2, shared_I=128), 0, 8),
     # down K = 2048: items of 10 .. 16 rows run one token tile, 17 .. 21 two
