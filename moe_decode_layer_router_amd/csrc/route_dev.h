@@ -420,51 +420,65 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
 // keeps every CU busy.
 //
 // Wave w takes tokens (w & 1) TT / 2 .. + TT / 2 and rows (w >> 1) 32 .. + 32:
-// NT = TT / 32 token tiles x 2 row tiles of 16 x 16. In a 16-K block a lane
-// loads 4 consecutive K of one router row (16 B) and of one token row (4
-// bf16); MFMA step s takes K index 4 (lane / 16) + s of the block in both
-// operands, so every product of the block is summed once. Block b accumulates
+// NT = TT / 32 token tiles x 2 row tiles of 16 x 16. In a block of KB = 4 KL
+// K a lane loads KL consecutive K of one router row (4 KL bytes) and of one
+// token row (KL bf16); MFMA step s takes K index KL (lane / 16) + s of the
+// block in both operands, so every product of the block is summed once. With
+// KL = 8 the 16 lanes of one K group read whole 128-byte lines of 16 rows.
+// Block b accumulates
 // into set b % 4; the sets are added as (0 + 1) + (2 + 3), which keeps the
 // sequential chains a quarter of the part. Rows past E and tokens past S
 // repeat the last one and are not stored.
 constexpr int kRouteTileE = 64;
 #ifndef MOE_ROUTE_RING
-#define MOE_ROUTE_RING 8
+#define MOE_ROUTE_RING (32 / MOE_ROUTE_KL)
 #endif
-constexpr int kRouteRing = MOE_ROUTE_RING;  // 16-K blocks in flight a wave
+constexpr int kRouteRing = MOE_ROUTE_RING;  // blocks in flight a wave
 
 template <int NT>
 struct RouteBlk {
-  f32x4_t w[2];   // 2 row tiles: 4 K of this lane's row
-  uint2 x[NT];    // NT token tiles: 4 bf16 of this lane's token
+  f32x4_t w[2][kRouteKL / 4];     // 2 row tiles: KL K of this lane's row
+  uint32_t x[NT][kRouteKL / 2];   // NT token tiles: KL bf16 of this lane's token
 };
 
 template <int NT>
 __device__ __forceinline__ void route_blk_load(RouteBlk<NT>& b, const float* const (&wrow)[2],
                                                const uint16_t* const (&xrow)[NT], int blk) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) b.w[i] = *reinterpret_cast<const f32x4_t*>(wrow[i] + 16 * blk);
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int j = 0; j < NT; ++j) b.x[j] = *reinterpret_cast<const uint2*>(xrow[j] + 16 * blk);
+    for (int v = 0; v < kRouteKL / 4; ++v)
+      b.w[i][v] = *reinterpret_cast<const f32x4_t*>(wrow[i] + kRouteKB * blk + 4 * v);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if constexpr (kRouteKL == 8) {
+      const uint4 u = *reinterpret_cast<const uint4*>(xrow[j] + kRouteKB * blk);
+      b.x[j][0] = u.x; b.x[j][1] = u.y; b.x[j][2] = u.z; b.x[j][3] = u.w;
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(xrow[j] + kRouteKB * blk);
+      b.x[j][0] = u.x; b.x[j][1] = u.y;
+    }
+  }
 }
 
 template <int NT>
 __device__ __forceinline__ void route_blk_mfma(const RouteBlk<NT>& b, f32x4_t (&acc)[2][NT]) {
-  float xf[NT][4];
+  float xf[NT][kRouteKL];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    xf[j][0] = bf16_lo(b.x[j].x);
-    xf[j][1] = bf16_hi(b.x[j].x);
-    xf[j][2] = bf16_lo(b.x[j].y);
-    xf[j][3] = bf16_hi(b.x[j].y);
-  }
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
-  for (int st = 0; st < 4; ++st)
+    for (int h = 0; h < kRouteKL / 2; ++h) {
+      xf[j][2 * h] = bf16_lo(b.x[j][h]);
+      xf[j][2 * h + 1] = bf16_hi(b.x[j][h]);
+    }
+#pragma unroll
+  for (int st = 0; st < kRouteKL; ++st)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.w[i][st], xf[j][st], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.w[i][st / 4][st % 4], xf[j][st],
+                                                           acc[i][j], 0, 0, 0);
 }
 
 // Workgroup (4 waves): tile (tt, et) of K part p.
@@ -480,7 +494,7 @@ __device__ __forceinline__ void router_split_tile(const uint16_t* __restrict__ x
   const int g = lane >> 4, c = lane & 15;
   const int t0 = tt * TT + (w & 1) * (TT / 2);
   const int e0 = et * kRouteTileE + (w >> 1) * 32;
-  const int k0 = p * Kp + 4 * g;
+  const int k0 = p * Kp + kRouteKL * g;
   const float* wrow[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -498,7 +512,7 @@ __device__ __forceinline__ void router_split_tile(const uint16_t* __restrict__ x
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[a][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nb = Kp / 16;
+  const int nb = Kp / kRouteKB;
   RouteBlk<NT> ring[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) route_blk_load(ring[i], wrow, xrow, min(i, nb - 1));
