@@ -14,7 +14,13 @@
 
 namespace moeblk {
 
-constexpr int kCombineThreads = 256;
+// threads a token's workgroup; combine us at 256 / 512 / 1024: S = 8
+// 4.00 / 3.96 / 5.23, S = 64 4.29 / 4.18 / 5.77, S = 128 (d = 7168)
+// 8.78 / 8.36 / 9.61
+#ifndef MOE_COMBINE_THREADS
+#define MOE_COMBINE_THREADS 512
+#endif
+constexpr int kCombineThreads = MOE_COMBINE_THREADS;
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -26,10 +32,11 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // for VPT in {1, 2, 4, 8}
 inline int combine_vpt(int d) {
   const int nvec = d / 8;
-  return nvec <= 256 ? 1 : nvec <= 512 ? 2 : nvec <= 1024 ? 4 : 8;
+  constexpr int T = kCombineThreads;
+  return nvec <= T ? 1 : nvec <= 2 * T ? 2 : nvec <= 4 * T ? 4 : 8;
 }
 
-// workgroup-wide sums of NB values at once (256 threads, one barrier pair),
+// workgroup-wide sums of NB values at once (kCombineThreads, one barrier pair),
 // every thread gets them; fixed order: the wave's butterfly, then the 4 waves
 template <int NB>
 __device__ __forceinline__ void block_sum_n(double (&v)[NB], double (*red)[kCombineThreads / kWave]) {
@@ -55,7 +62,7 @@ __device__ __forceinline__ void block_sum_n(double (&v)[NB], double (*red)[kComb
 // at d = 7168, not at d <= 4096)
 template <int VPT>
 constexpr int combine_batch() {
-  return VPT == 4 ? 2 : 1;
+  return VPT * kCombineThreads == 1024 ? 2 : 1;
 }
 
 // token t: out[t] = sum over slots s with pick_pos >= 0 of
