@@ -121,7 +121,8 @@ def test_route_rejects():
 
 def test_route_workspace():
     """S <= 32 needs no scratch; beyond, the router's K parts [P, S, E] fp32
-    with P a power of two up to 32 that divides d / 16."""
+    with P a power of two up to 32 that divides d / 32: every part is a whole
+    number of the kernel's 32-K blocks, for every d the dims allow."""
     assert mb.moe_route_workspace_bytes(dims(S=16)) == 0
     assert mb.moe_route_workspace_bytes(dims(S=32)) == 0
     assert mb.moe_route_workspace_bytes(dims(S=0)) == 0
@@ -129,7 +130,12 @@ def test_route_workspace():
         n = mb.moe_route_workspace_bytes(dims(S=S, d=d, E=E, n_local=min(E, 8), topk=2))
         P = n // (S * E * 4)
         assert n == P * S * E * 4 or (n - P * S * E * 4) < 256
-        assert P >= 1 and P & (P - 1) == 0 and P <= 32 and (d // 16) % P == 0, (S, d, E, P)
+        assert P >= 1 and P & (P - 1) == 0 and P <= 32 and (d // 32) % P == 0, (S, d, E, P)
+    for S in (33, 64, 65, 128):
+        for d in range(128, 16385, 128):
+            n = mb.moe_route_workspace_bytes(dims(S=S, d=d, E=256, n_local=32, topk=8))
+            P = n // (S * 256 * 4)
+            assert P >= 1 and P & (P - 1) == 0 and (d // P) % 32 == 0, (S, d, P)
     wd = ctypes.byref(dims(S=64, d=4096, E=256, n_local=32, topk=8))
     need = mb.moe_route_workspace_bytes(dims(S=64, d=4096, E=256, n_local=32, topk=8))
     ok = [FAKE] * 6
