@@ -65,6 +65,10 @@ def _declare(L):
     L.orc_latent_norm.argtypes = [_I, _I, ctypes.c_double, _P, _P, _P]
     L.orc_post_proj.argtypes = [_I, _I, _I, _P, _P, _P]
     L.orc_forward.argtypes = [_I] * 8 + [_F, _I, _I] + [_P] * 20
+    L.orc_set_threads.argtypes = [_I]
+    L.orc_set_threads.restype = None
+    L.orc_max_threads.argtypes = []
+    L.orc_max_threads.restype = _I
     for f in (
         "orc_router_logits",
         "orc_route_weights",
@@ -102,6 +106,18 @@ def _chk(rc, name):
 
 def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------- threads
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the batch functions (results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ---------------------------------------------------------------- scalars

@@ -24,6 +24,7 @@ def build_oracle(verbose: bool = False) -> str:
         "-fno-fast-math",
         "-D_GNU_SOURCE",
         "-Wall",
+        "-fopenmp",
         "-o",
         LIB + ".tmp",
         SRC,

@@ -53,12 +53,23 @@
  * library routines and brute force; see the tests for which pin covers what.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORC_OK 0
 #define ORC_EINVAL (-1)
+
+/* Threads: the batch functions (router logits, top-k, the expert FFN over
+ * bucket rows, the combine over tokens, the projections) and the rows of one
+ * GEMV run their independent outputs on OpenMP threads; every output value
+ * is still computed by one thread in the order written below, so results do
+ * not depend on the thread count. */
+void orc_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* bf16 <-> fp64                                                             */
@@ -111,11 +122,17 @@ double orc_e8m0(unsigned x) {
 }
 
 /* Element k of one MXFP4 row: nibble k (low nibble of byte k/2 for even k),
- * scaled by scale byte k/32. */
+ * scaled by scale byte k/32, as the number the expert GEMMs multiply. The K3
+ * page (stages "C, D") decodes MXFP4 in registers into the bf16 operands of
+ * the MFMA; bf16 and fp32 share one exponent range, and an e2m1 value times
+ * 2^(X-127) has at most two significant bits and lies at or above 2^-128, so
+ * the decoded value is exact in either format unless its magnitude reaches
+ * 2^128 (scale bytes 253 and 254), where it overflows to infinity. Rounding
+ * the exact product to fp32 states exactly that. */
 double orc_mx_elem(const uint8_t* q_row, const uint8_t* s_row, long k) {
   uint8_t byte = q_row[k >> 1];
   unsigned nib = (k & 1) ? (byte >> 4) : (byte & 0xFu);
-  return orc_e2m1(nib) * orc_e8m0(s_row[k >> 5]);
+  return (double)(float)(orc_e2m1(nib) * orc_e8m0(s_row[k >> 5]));
 }
 
 /* ------------------------------------------------------------------------ */
@@ -126,6 +143,7 @@ double orc_mx_elem(const uint8_t* q_row, const uint8_t* s_row, long k) {
 int orc_router_logits(int S, int d, int E, const uint16_t* x, const float* wr,
                       const float* bias, double* logits) {
   if (S < 0 || d <= 0 || E <= 0 || !x || !wr || !logits) return ORC_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
   for (int t = 0; t < S; ++t)
     for (int e = 0; e < E; ++e) {
       double acc = 0.0;
@@ -256,6 +274,7 @@ int orc_mx_gate_up(int d, int I, const uint16_t* x, const uint8_t* w13q, const u
   if (d <= 0 || I <= 0 || (d % 32) || !x || !w13q || !w13s || !h) return ORC_EINVAL;
   uint16_t* gu = (uint16_t*)malloc(sizeof(uint16_t) * 2 * (size_t)I);
   if (!gu) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
   for (int n = 0; n < 2 * I; ++n) {
     const uint8_t* qr = w13q + (long)n * (d / 2);
     const uint8_t* sr = w13s + (long)n * (d / 32);
@@ -277,6 +296,7 @@ int orc_mx_gate_up(int d, int I, const uint16_t* x, const uint8_t* w13q, const u
 int orc_mx_down(int d, int I, const uint16_t* h, const uint8_t* w2q, const uint8_t* w2s,
                 uint16_t* y) {
   if (d <= 0 || I <= 0 || (I % 32) || !h || !w2q || !w2s || !y) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
   for (int c = 0; c < d; ++c) {
     const uint8_t* qr = w2q + (long)c * (I / 2);
     const uint8_t* sr = w2s + (long)c * (I / 32);
@@ -308,6 +328,7 @@ int orc_bf_gate_up(int d, int Is, const uint16_t* x, const uint16_t* ws13, uint1
   if (d <= 0 || Is <= 0 || !x || !ws13 || !h) return ORC_EINVAL;
   uint16_t* gu = (uint16_t*)malloc(sizeof(uint16_t) * 2 * (size_t)Is);
   if (!gu) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
   for (int n = 0; n < 2 * Is; ++n) {
     double acc = 0.0;
     for (int j = 0; j < d; ++j)
@@ -325,6 +346,7 @@ int orc_bf_gate_up(int d, int Is, const uint16_t* x, const uint16_t* ws13, uint1
 
 int orc_bf_down(int d, int Is, const uint16_t* h, const uint16_t* ws2, uint16_t* y) {
   if (d <= 0 || Is <= 0 || !h || !ws2 || !y) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
   for (int c = 0; c < d; ++c) {
     double acc = 0.0;
     for (int i = 0; i < Is; ++i)
@@ -356,27 +378,48 @@ int orc_expert_ffn(int S, int d, int I, int n_loc, int topk, int Is, const uint1
                    const int32_t* rows, const uint16_t* ws13, const uint16_t* ws2,
                    uint16_t* y) {
   if (S < 0 || !x || !counts || !offsets || !rows || !y) return ORC_EINVAL;
+  if (Is > 0 && (!ws13 || !ws2)) return ORC_EINVAL;
   int kk = topk < n_loc ? topk : n_loc;
   long R_max = (long)S * kk;
   size_t e13q = (size_t)2 * I * (d / 2), e13s = (size_t)2 * I * (d / 32);
   size_t e2q = (size_t)d * (I / 2), e2s = (size_t)d * (I / 32);
+  /* the bucket rows to run, with their experts (checked before any work) */
+  long n_rows = 0;
+  for (int el = 0; el < n_loc; ++el) {
+    if (counts[el] < 0 || offsets[el] < 0 || offsets[el] + counts[el] > R_max) return ORC_EINVAL;
+    n_rows += counts[el];
+  }
+  int32_t* row_el = (int32_t*)malloc(sizeof(int32_t) * (size_t)(2 * n_rows + 1));
+  if (!row_el) return ORC_EINVAL;
+  int32_t* row_r = row_el + n_rows;
+  long i = 0;
   for (int el = 0; el < n_loc; ++el)
     for (int r = offsets[el]; r < offsets[el] + counts[el]; ++r) {
-      int t = rows[r];
-      if (t < 0 || t >= S || r >= R_max) return ORC_EINVAL;
-      int rc = orc_expert_row(d, I, x + (long)t * d, w13q + el * e13q, w13s + el * e13s,
-                              w2q + el * e2q, w2s + el * e2s, NULL, NULL, y + (long)r * d);
-      if (rc) return rc;
+      if (rows[r] < 0 || rows[r] >= S) {
+        free(row_el);
+        return ORC_EINVAL;
+      }
+      row_el[i] = el;
+      row_r[i++] = r;
     }
-  if (Is > 0) {
-    if (!ws13 || !ws2) return ORC_EINVAL;
-    for (int t = 0; t < S; ++t) {
-      int rc = orc_shared_row(d, Is, x + (long)t * d, ws13, ws2, NULL, NULL,
-                              y + (R_max + t) * d);
-      if (rc) return rc;
+  /* every bucket row, then every token through the shared expert: independent
+   * rows, one thread each */
+  long n_tasks = n_rows + (Is > 0 ? S : 0);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (long j = 0; j < n_tasks; ++j) {
+    if (j < n_rows) {
+      int el = row_el[j], r = row_r[j], t = rows[r];
+      bad |= orc_expert_row(d, I, x + (long)t * d, w13q + el * e13q, w13s + el * e13s,
+                            w2q + el * e2q, w2s + el * e2s, NULL, NULL, y + (long)r * d) != 0;
+    } else {
+      int t = (int)(j - n_rows);
+      bad |= orc_shared_row(d, Is, x + (long)t * d, ws13, ws2, NULL, NULL,
+                            y + (R_max + t) * d) != 0;
     }
   }
-  return ORC_OK;
+  free(row_el);
+  return bad ? ORC_EINVAL : ORC_OK;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -405,23 +448,23 @@ int orc_combine(int S, int d, int topk, int n_loc, int Is, float eps, const uint
   if (S < 0 || d <= 0 || !y || !w || !pick_pos || !out) return ORC_EINVAL;
   int kk = topk < n_loc ? topk : n_loc;
   long R_max = (long)S * kk;
-  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
-  double* z = (double*)malloc(sizeof(double) * (size_t)d);
-  if (!acc || !z) {
-    free(acc);
-    free(z);
-    return ORC_EINVAL;
-  }
+  for (long p = 0; p < (long)S * topk; ++p)
+    if (pick_pos[p] >= R_max) return ORC_EINVAL;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
   for (int t = 0; t < S; ++t) {
+    double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+    double* z = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!acc || !z) {
+      free(acc);
+      free(z);
+      bad = 1;
+      continue;
+    }
     for (int c = 0; c < d; ++c) acc[c] = 0.0;
     for (int i = 0; i < topk; ++i) {
       int p = pick_pos[t * topk + i];
       if (p < 0) continue;
-      if (p >= R_max) {
-        free(acc);
-        free(z);
-        return ORC_EINVAL;
-      }
       orc_norm_row(d, y + (long)p * d, gamma, (double)eps, z);
       double wt = (double)w[t * topk + i];
       for (int c = 0; c < d; ++c) acc[c] += wt * z[c];
@@ -429,10 +472,10 @@ int orc_combine(int S, int d, int topk, int n_loc, int Is, float eps, const uint
     if (Is > 0)
       for (int c = 0; c < d; ++c) acc[c] += orc_bf16_to_f64(y[(R_max + t) * d + c]);
     for (int c = 0; c < d; ++c) out[(long)t * d + c] = (float)acc[c];
+    free(acc);
+    free(z);
   }
-  free(acc);
-  free(z);
-  return ORC_OK;
+  return bad ? ORC_EINVAL : ORC_OK;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -449,6 +492,7 @@ int orc_combine(int S, int d, int topk, int n_loc, int Is, float eps, const uint
 /* out[t][n] = bf16( sum_k in[t][k] * w[n][k] ), in [S][K] and w [N][K] bf16 */
 int orc_dense_proj(int S, int K, int N, const uint16_t* in, const uint16_t* w, uint16_t* out) {
   if (S < 0 || K <= 0 || N <= 0 || !in || !w || !out) return ORC_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
   for (int t = 0; t < S; ++t)
     for (int n = 0; n < N; ++n) {
       double acc = 0.0;
@@ -464,6 +508,7 @@ int orc_dense_proj(int S, int K, int N, const uint16_t* in, const uint16_t* w, u
 int orc_latent_norm(int S, int L, double eps, const uint16_t* h_raw, const uint16_t* gamma,
                     uint16_t* h) {
   if (S < 0 || L <= 0 || !h_raw || !h) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
   for (int t = 0; t < S; ++t) {
     double ss = 0.0;
     for (int c = 0; c < L; ++c) {

@@ -64,7 +64,13 @@ def decode_mx(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     hi = tab[q >> 4]
     el = np.stack([lo, hi], axis=-1).reshape(*q.shape[:-1], q.shape[-1] * 2)
     scale = np.ldexp(1.0, s.astype(np.int64) - 127)
-    return el * np.repeat(scale, 32, axis=-1)
+    scale = np.where(s == 0xFF, np.nan, scale)  # e8m0 0xFF: NaN (OCP MX v1.0)
+    v = el * np.repeat(scale, 32, axis=-1)
+    # the decoded weight is an fp32 / bf16 operand: magnitudes from 2^128 on
+    # (binary32's largest finite value is (2 - 2^-23) 2^127) are infinite
+    with np.errstate(invalid="ignore"):
+        big = np.abs(v) >= 2.0**128
+    return np.where(big, np.copysign(np.inf, v), v)
 
 
 def silu_hp(g) -> np.ndarray:

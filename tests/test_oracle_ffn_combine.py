@@ -188,3 +188,23 @@ def test_shared_row_matches_dense_numpy():
     hh = nearest_bf16_bits(silu_hp(bf16_val(g[:Is])) * bf16_val(g[Is:]))
     assert np.array_equal(h, hh)
     assert np.array_equal(y, nearest_bf16_bits(bf16_val(ws2) @ bf16_val(hh)))
+
+
+def test_thread_count_does_not_change_results():
+    """The batch functions split independent outputs over threads; each value
+    is computed by one thread in the written order, so 1 thread and many
+    threads give the same bits."""
+    from synth import get_config, make_inputs
+
+    inp = make_inputs(get_config("tiny").with_(S=24, E=16, n_local=8, topk=4, shared_I=128), 4,
+                      gamma="random")
+    n = oracle.max_threads()
+    try:
+        oracle.set_threads(1)
+        a = oracle.forward(inp)
+        oracle.set_threads(max(n, 4))
+        b = oracle.forward(inp)
+    finally:
+        oracle.set_threads(n)
+    for k in ("logits", "ids", "w", "rows", "y", "out"):
+        assert np.array_equal(a[k], b[k]), k

@@ -117,3 +117,39 @@ def test_mx_round_trip_every_code_and_scale():
             scale = 2.0 ** (x - 127)
             cands = [c for c in range(16) if tab[c] * scale == v and math.copysign(1, tab[c]) == math.copysign(1, v)]
             assert cands == [code], (x, code, v)
+
+
+# IEEE 754 binary32: the largest finite value is (2 - 2^-23) 2^127, so a
+# magnitude of 2^128 or more is out of range; 2^-149 is the smallest subnormal.
+@pytest.mark.parametrize(
+    "code,x,want",
+    [
+        (0x1, 0, 2.0**-128),  # 0.5 x 2^-127: a subnormal, exact
+        (0x9, 0, -(2.0**-128)),
+        (0x7, 0, 6 * 2.0**-127),
+        (0x3, 1, 1.5 * 2.0**-126),
+        (0x7, 252, 6 * 2.0**125),  # 1.5 x 2^127: the largest finite decoded value
+        (0x5, 253, 3 * 2.0**126),  # 1.5 x 2^127 again
+        (0x6, 253, float("inf")),  # 4 x 2^126 = 2^128: out of range
+        (0xE, 253, float("-inf")),
+        (0x7, 253, float("inf")),
+        (0x3, 254, 1.5 * 2.0**127),
+        (0x4, 254, float("inf")),  # 2 x 2^127
+        (0xC, 254, float("-inf")),
+        (0x0, 254, 0.0),
+    ],
+)
+def test_mx_elem_range_ends(code, x, want):
+    """The decoded weight is a value of the MFMA's operand format: every
+    e2m1 x 2^(X-127) is exact there except magnitudes >= 2^128, which
+    overflow to infinity (scale bytes 253 and 254)."""
+    v = oracle.mx_elem(np.array([code], np.uint8), np.array([x], np.uint8), 0)
+    assert v == want and math.copysign(1, v) == math.copysign(1, want), (code, x, v)
+
+
+def test_mx_elem_nan_scale_is_nan_for_every_code():
+    """e8m0 0xFF is NaN (OCP MX v1.0): all 32 elements of its block are NaN,
+    zeros included."""
+    for code in range(16):
+        v = oracle.mx_elem(np.array([code], np.uint8), np.array([255], np.uint8), 0)
+        assert math.isnan(v), code
