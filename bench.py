@@ -5,8 +5,11 @@ A step is one pass of the whole block -- route, bucket, expert FFN, combine --
 over one batch of S token rows, all inputs resident in HBM. It is timed as the
 library's one-call entry point moe_forward (the headline `value`) and, for
 comparison, as the four calls moe_route -> moe_bucket -> moe_expert_ffn ->
-moe_combine. The default workload is S = 8, d = 4096, 256 experts (32 local),
-I = 2048, top-8 uniform routing ("s8_uniform").
+moe_combine. The headline workload is the largest of the row counts the
+metric spans: S = 128, d = 7168, 256 experts (32 local), I = 2048, top-8
+uniform routing, plus the always-on dense bf16 shared expert
+("s128_shared"). The S = 8, 16 and 64 workloads ride along under
+``workloads`` (same protocol, fewer steps).
 
 Last-level-cache control: MI355X's 256 MB Infinity Cache would hold one
 step's active weights (about 94 MB here), so the benchmark keeps R copies of
@@ -21,7 +24,9 @@ kernel), timed with HIP events around each call on the stream its
 kernels run on, in a separate timed pass; its
 ``traffic`` comes from the committed rocprofv3 counter summary when that
 summary was taken on the current kernel sources, else null.
-``cpu_baseline`` times the CPU oracle on the same workload.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload (its first k token rows), with all of the host's OpenMP threads and
+with one thread (``single_thread``).
 ``around_block`` times the steps next to the block (moe_pre_expert,
 moe_latent_norm, moe_post_expert) at one GPU's share of their shapes.
 """
@@ -74,27 +79,65 @@ def expert_bytes(cfg) -> int:
     return 3 * cfg.I * cfg.d * 17 // 32
 
 
-def cpu_baseline(inp, budget_s: float) -> dict:
-    """The CPU oracle (single thread, as it stands) on whole steps of the same
-    workload until about budget_s seconds have passed (at least one step)."""
+def _oracle_tokens(inp, k: int) -> dict:
+    """The workload's inputs cut to its first k token rows: same weights,
+    router and routing structure, fewer rows."""
+    cfg = inp["cfg"]
+    sub = dict(inp)
+    sub["cfg"] = cfg.with_(S=k)
+    sub["x"] = inp["x"][:k]
+    return sub
+
+
+def _time_oracle(inp, k: int, budget_s: float):
+    """Whole oracle steps (route, bucket, expert FFN, combine) over the first
+    k tokens, repeated until about budget_s seconds: (tokens/s, steps, s)."""
     import oracle
 
-    cfg = inp["cfg"]
+    sub = _oracle_tokens(inp, k)
     n, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(inp)
+        oracle.forward(sub)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or el / n * (n + 1) > 2.5 * budget_s:
             break
-    return {
-        "value": round(cfg.S * n / el, 3),
-        "unit": "tokens/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"{n} whole steps of {cfg.name} (S={cfg.S}) on the same inputs, single thread, "
-        f"{el:.1f} s",
-    }
+    return k * n / el, n, el
+
+
+def cpu_baseline(inp, budget_s: float) -> dict:
+    """The CPU oracle as it stands, on this host's cores: all the threads
+    OpenMP gives it (the headline) and one thread. A bounded sample: whole
+    oracle steps over the workload's first k token rows, k doubled from 1
+    until one step takes a quarter of budget_s (or k = S), then steps of k rows
+    repeated for about budget_s seconds; tokens/s = k x steps / time."""
+    import oracle
+
+    cfg = inp["cfg"]
+    res = {}
+    n_thr = oracle.max_threads()
+    for mode, threads in (("all", n_thr), ("single", 1)):
+        oracle.set_threads(threads)
+        k = 1
+        while k < cfg.S:
+            _, _, el1 = _time_oracle(inp, k, 0.0)  # one step
+            if el1 >= budget_s / 4:
+                break
+            k = min(cfg.S, 2 * k)
+        rate, n, el = _time_oracle(inp, k, budget_s)
+        res[mode] = {
+            "value": round(rate, 3),
+            "unit": "tokens/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} oracle steps over the first {k} of {cfg.S} token rows of {cfg.name} "
+            f"(same weights and routing), {threads} thread{'s' if threads > 1 else ''}, {el:.1f} s",
+        }
+    oracle.set_threads(n_thr)
+    out = dict(res["all"])
+    out["host_cpu_count"] = os.cpu_count()
+    out["single_thread"] = res["single"]
+    return out
 
 
 def around_block(S: int, warmup: int, K: int) -> dict:
@@ -113,7 +156,7 @@ def around_block(S: int, warmup: int, K: int) -> dict:
     n = max(1, math.ceil(2 * LLC_BYTES / b_w))
     st.add_weight_copies(n - 1)
     torch.cuda.synchronize()
-    res = {"workload": f"latent_s{S}: {pc.desc}", "weight_copies_rotated": n}
+    res = {"workload": f"latent_s{S}: S={S}, {pc.desc.split(', ', 1)[1]}", "weight_copies_rotated": n}
     steps = {
         "pre": (st.pre, pc.n_pre * pc.D * 2 + pc.e_router * pc.D * 4 + S * pc.D * 2 + S * pc.n_pre * 2
                 + S * pc.e_router * 4),
@@ -153,37 +196,15 @@ def around_block(S: int, warmup: int, K: int) -> dict:
     return res
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    # a shorter warm-up leaves the first timed pass a few percent slow at S = 128
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="s8_uniform")
-    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run a plain device copy of this size (counter calibration)")
-    ap.add_argument("--no-around", action="store_true", help="skip the steps around the block")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(
-            f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU's share of the "
-            "expert-parallel block (no collectives); run with --gpus 1",
-            file=sys.stderr,
-        )
-        return 2
-
+def measure(cfg, K: int, warmup: int, copies_arg: int = 0, calib_copy_mib: int = 0) -> dict:
+    """Time one workload: moe_forward steps (the headline), the four calls,
+    per-step spread, the warm-cache pass and each expert-FFN call."""
     import torch
 
     from moe_decode_layer_router_amd.block import MoeBlock
-    from synth import get_config, make_inputs
+    from synth import make_inputs
 
-    cfg = get_config(args.workload)
     inp = make_inputs(cfg, 0)
-    torch.cuda.set_device(0)
     blk = MoeBlock(inp, device="cuda:0")
     blk.forward(0)
     torch.cuda.synchronize()
@@ -194,12 +215,12 @@ def main() -> int:
     b_router = cfg.E * cfg.d * 4
     b_shared = 3 * cfg.shared_I * cfg.d * 2
     b_step_w = b_mx + b_router + b_shared
-    copies = args.copies or max(1, math.ceil(2 * LLC_BYTES / max(b_mx + b_shared, 1)))
+    copies = copies_arg or max(1, math.ceil(2 * LLC_BYTES / max(b_mx + b_shared, 1)))
     blk.add_weight_copies(copies - 1)
     torch.cuda.synchronize()
 
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * 2**20 // 4
+    if calib_copy_mib:
+        n = calib_copy_mib * 2**20 // 4
         a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
         b = torch.empty_like(a)
         for _ in range(3):
@@ -207,10 +228,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    K = args.steps
-
     def timed(fn) -> float:
-        for i in range(args.warmup):
+        for i in range(warmup):
             fn(i % copies)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
@@ -225,7 +244,7 @@ def main() -> int:
     def per_call(fn, n):
         """Event pairs around each of n calls on the current stream -> ms each."""
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for i in range(min(args.warmup, n)):
+        for i in range(min(warmup, n)):
             fn(i % copies)
         torch.cuda.synchronize()
         for i in range(n):
@@ -260,16 +279,88 @@ def main() -> int:
     # without a shared expert: one launch; else gate_up, then down
     single = not cfg.shared_I
     ffn_kernels = "moe_expert_ffn: " + ("ffn_single_kernel" if single else "gate_up_kernel + down_kernel")
+    del blk
+    torch.cuda.empty_cache()
+    return dict(
+        inp=inp, ms=ms, ms4=ms4, st=st, ms_warm=ms_warm, ffn_ms=ffn_ms, b_ffn=b_ffn, b_mx=b_mx,
+        b_step_w=b_step_w, achieved=achieved, ffn_kernels=ffn_kernels, n_active=n_active,
+        picks=picks, copies=copies,
+    )
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    # a shorter warm-up leaves the first timed pass a few percent slow at S = 128
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="s128_shared")
+    ap.add_argument("--also", default="s8_uniform,s16_local25,s64_zipf",
+                    help="more workloads timed beside the headline (comma list, '' for none)")
+    ap.add_argument("--also-steps", type=int, default=100)
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="per oracle mode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-around", action="store_true", help="skip the steps around the block")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(
+            f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU's share of the "
+            "expert-parallel block (no collectives); run with --gpus 1",
+            file=sys.stderr,
+        )
+        return 2
+
+    import torch
+
+    from synth import get_config
+
+    torch.cuda.set_device(0)
+    cfg = get_config(args.workload)
+    r = measure(cfg, args.steps, args.warmup, args.copies, args.calib_copy_mib)
+    ms, K = r["ms"], args.steps
     traffic = committed_traffic(cfg.name)
 
     # read bandwidth of a torch reduction over 1 GiB (context only: not a
     # tuned streaming kernel)
     big = torch.ones(2**28, dtype=torch.float32, device="cuda:0")
-    rd = per_call(lambda _i: big.sum(), 20)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in evs:
+        a.record()
+        big.sum()
+        b.record()
+    torch.cuda.synchronize()
+    rd = sorted(a.elapsed_time(b) for a, b in evs)
     read_gbps = big.numel() * 4 / (rd[len(rd) // 2] * 1e-3) / 1e9
     del big
 
     around = None if args.no_around else around_block(cfg.S, args.warmup, K)
+
+    def summary(c, m) -> dict:
+        return {
+            "S": c.S,
+            "ms_per_step": round(m["ms"], 5),
+            "tokens_per_s": round(c.S / (m["ms"] * 1e-3), 1),
+            "all_weight_pct_hbm_peak": round(100 * m["b_step_w"] / (m["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "mxfp4_weight_gbps": round(m["b_mx"] / (m["ms"] * 1e-3) / 1e9, 1),
+            "four_call_ms_per_step": round(m["ms4"], 5),
+            "active_local_experts": m["n_active"],
+            "ffn_kernel": m["ffn_kernels"],
+            "ffn_avg_ms": round(m["ffn_ms"], 5),
+            "ffn_frac_hbm_peak": round(m["achieved"] / HBM_PEAK_GBPS, 4),
+            "weight_copies_rotated": m["copies"],
+        }
+
+    others = {}
+    for name in [w for w in args.also.split(",") if w and w != cfg.name]:
+        c = get_config(name)
+        m = measure(c, args.also_steps, min(args.warmup, args.also_steps))
+        others[name] = summary(c, m)
+        del m
 
     tok_s = cfg.S / (ms * 1e-3)
     line = {
@@ -294,34 +385,35 @@ def main() -> int:
             "I": cfg.I,
             "topk": cfg.topk,
             "shared_I": cfg.shared_I,
-            "active_local_experts": n_active,
-            "local_picks": picks,
-            "weight_copies_rotated": copies,
+            "active_local_experts": r["n_active"],
+            "local_picks": r["picks"],
+            "weight_copies_rotated": r["copies"],
         },
-        "mxfp4_weight_gbps": round(b_mx / (ms * 1e-3) / 1e9, 1),
-        "all_weight_pct_hbm_peak": round(100 * b_step_w / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-        "four_call_ms_per_step": round(ms4, 5),
-        "step_ms_median": round(st[len(st) // 2], 5),
-        "step_ms_p10": round(st[len(st) // 10], 5),
-        "step_ms_p90": round(st[(9 * len(st)) // 10], 5),
-        "warm_llc_ms_per_step": round(ms_warm, 5),
+        "mxfp4_weight_gbps": round(r["b_mx"] / (ms * 1e-3) / 1e9, 1),
+        "all_weight_pct_hbm_peak": round(100 * r["b_step_w"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "four_call_ms_per_step": round(r["ms4"], 5),
+        "step_ms_median": round(r["st"][len(r["st"]) // 2], 5),
+        "step_ms_p10": round(r["st"][len(r["st"]) // 10], 5),
+        "step_ms_p90": round(r["st"][(9 * len(r["st"])) // 10], 5),
+        "warm_llc_ms_per_step": round(r["ms_warm"], 5),
         "torch_sum_read_gbps": round(read_gbps, 1),
         "roofline": {
-            "kernel": ffn_kernels,
+            "kernel": r["ffn_kernels"],
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": round(r["achieved"], 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": b_ffn,
-            "avg_ms": round(ffn_ms, 5),
+            "algorithmic_bytes": r["b_ffn"],
+            "avg_ms": round(r["ffn_ms"], 5),
         },
         "cpu_baseline": None,
+        "workloads": others,
         "around_block": around,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(r["inp"], args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -201,6 +201,12 @@ size_t moe_ffn_workspace_bytes(const moe_dims* dims);
  *              a call in which a wait hit its time bound (a correct run never
  *              does; that call's outputs are undefined and the workspace must
  *              be zero-filled again).
+ * MXFP4 decode: element = e2m1 value x 2^(X - 127) for the block's e8m0 byte
+ * X, as a bf16 operand; every byte is accepted: X = 0 scales by 2^-127 (bf16
+ * subnormals are kept), X = 0xFF makes the block's 32 elements NaN (OCP MX
+ * v1.0), and at X = 253 / 254 decoded magnitudes of 2^128 and more are +-inf.
+ * NaNs and infinities then propagate by IEEE rules (a row's sum of squares
+ * in moe_combine included).
  * The down GEMM of an expert needs all of its SwiGLU rows (K3 page, stages
  * "C, D"). Without a shared expert the FFNs are one launch: a down task
  * issues its first weight loads, then waits on a ready flag set once all of

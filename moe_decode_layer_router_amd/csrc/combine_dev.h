@@ -37,7 +37,8 @@ inline int combine_vpt(int d) {
 }
 
 // workgroup-wide sums of NB values at once (kCombineThreads, one barrier pair),
-// every thread gets them; fixed order: the wave's butterfly, then the 4 waves
+// every thread gets them; fixed order: the wave's butterfly, then the
+// kCombineThreads / 64 waves in order
 template <int NB>
 __device__ __forceinline__ void block_sum_n(double (&v)[NB], double (*red)[kCombineThreads / kWave]) {
 #pragma unroll
@@ -65,6 +66,103 @@ constexpr int combine_batch() {
   return VPT * kCombineThreads == 1024 ? 2 : 1;
 }
 
+// combine_token for d > 8192 (8 vectors a thread): the slots one at a time,
+// their pick positions and weights read where they are used, gamma and the
+// shared row read at use, so that the registers hold the accumulators and one
+// y row. (Holding gamma, the shared row and the unrolled slots' state as well
+// spilled 228 bytes a lane to scratch.) Same arithmetic, in the same order.
+template <int VPT, bool kCoh>
+__device__ __forceinline__ void combine_token_wide(const uint16_t* __restrict__ y,
+                                                   const float* __restrict__ tw,
+                                                   const int32_t* __restrict__ pick_pos,
+                                                   const uint16_t* __restrict__ gamma,
+                                                   float* __restrict__ out, int d, int topk,
+                                                   float eps, long shared_row0, int t,
+                                                   double (*red)[kCombineThreads / kWave]) {
+  const int nvec = d / 8;
+  float acc[VPT][8];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+  __amdgpu_buffer_rsrc_t yr;
+  if constexpr (kCoh)
+    yr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(y), 0, 0x7fffffff, 0x00020000);
+  const double inv_d = 1.0 / static_cast<double>(d);
+#pragma unroll 1
+  for (int s = 0; s < topk; ++s) {
+    const int p = pick_pos[static_cast<size_t>(t) * topk + s];  // the same in every thread
+    if (p < 0) continue;
+    const float wt = tw[static_cast<size_t>(t) * topk + s];
+    u32x4_t q[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = threadIdx.x + kCombineThreads * i;
+      q[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (v < nvec) {
+        if constexpr (kCoh)
+          q[i] = __builtin_amdgcn_raw_buffer_load_b128(
+              yr, static_cast<uint32_t>((static_cast<size_t>(p) * d + 8 * v) * 2), 0, kCpolSc1);
+        else
+          q[i] = *reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(p) * d + 8 * v);
+      }
+    }
+    double ss[1] = {0.0};
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double lo = bf16_lo(q[i][j]), hi = bf16_hi(q[i][j]);
+        ss[0] += lo * lo;
+        ss[0] += hi * hi;
+      }
+    block_sum_n<1>(ss, red);
+    // the row's values are widened to fp64 again below instead of keeping
+    // the widened copies of the sum of squares live (128 more registers)
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) asm volatile("" : "+v"(q[i]));
+    const double r = 1.0 / sqrt(ss[0] * inv_d + static_cast<double>(eps));
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = threadIdx.x + kCombineThreads * i;
+      float g[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g[j] = 1.0f;
+      if (gamma && v < nvec) {
+        const uint4 gv = *reinterpret_cast<const uint4*>(gamma + 8 * v);
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          g[2 * j] = bf16_lo(gw[j]);
+          g[2 * j + 1] = bf16_hi(gw[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][2 * j] += wt * (static_cast<float>(bf16_lo(q[i][j]) * r) * g[2 * j]);
+        acc[i][2 * j + 1] += wt * (static_cast<float>(bf16_hi(q[i][j]) * r) * g[2 * j + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = threadIdx.x + kCombineThreads * i;
+    if (v >= nvec) continue;
+    if (shared_row0 >= 0) {
+      const u32x4_t sh =
+          *reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(shared_row0 + t) * d + 8 * v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][2 * j] += bf16_lo(sh[j]);
+        acc[i][2 * j + 1] += bf16_hi(sh[j]);
+      }
+    }
+    float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * d + 8 * v);
+    o[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    o[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+  }
+}
+
 // token t: out[t] = sum over slots s with pick_pos >= 0 of
 //   w[t][s] * y[p] / sqrt(mean(y[p]^2) + eps) * gamma  (+ y[shared_row0 + t]).
 // The token's pick positions and weights are loaded first, then the y rows of
@@ -80,6 +178,10 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y,
                                               float* __restrict__ out, int d, int topk, float eps,
                                               long shared_row0, int t,
                                               double (*red)[kCombineThreads / kWave]) {
+  if constexpr (VPT >= 8) {
+    combine_token_wide<VPT, kCoh>(y, tw, pick_pos, gamma, out, d, topk, eps, shared_row0, t, red);
+    return;
+  }
   constexpr int NB = combine_batch<VPT>();
   const int nvec = d / 8;
   int pp[8];

@@ -73,11 +73,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ---------------------------------------------------------------- MXFP4
 
-// e8m0 byte -> the fp32 scale operand of the scaled fp4 converts: 2^(x - 127)
-// for x in 1..254 (exponent field x, zero mantissa).
+// e8m0 byte -> the fp32 scale operand of the scaled fp4 converts: the byte
+// in the exponent field, zero mantissa. The converts read only that field as
+// an e8m0 scale (measured on MI355X for every byte and code, through an MFMA
+// read-back): byte 0 scales by 2^-127 (0.5 decodes to the bf16 subnormal
+// 2^-128), 255 makes every element NaN, and at bytes 253 and 254 a decoded
+// magnitude of 2^128 or more becomes +-inf (bf16 has fp32's exponent range).
 __device__ __forceinline__ float e8m0_scale(uint32_t x) { return __uint_as_float(x << 23); }
 
 // 8 e2m1 codes (one dword, low nibble first) times `scale` -> 8 bf16, in K order.
+// Feeding MFMA operands, this compiles to four converts with the four byte
+// selects. (A probe that stored the 8 results to memory one by one compiled
+// to a single convert whose first element was copied to all 8; such uses need
+// their assembly checked.)
 __device__ __forceinline__ bf16x8_t decode_fp4x8(uint32_t w, float scale) {
   const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
   const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);

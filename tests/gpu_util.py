@@ -18,9 +18,9 @@ Tolerances (derived from the arithmetic; every comparison states its own):
   gate_up + SwiGLU (compare_h), then the GPU's y against the oracle's down GEMM
   applied to the GPU's own h (compare_y_step); the bounds are stated there;
 * combine alone (same y): fp32 against fp64, max |d out| <= 1e-5 RMS(out);
-* end to end: max |d out| <= 2e-2 RMS(out_oracle) over the compared rows on
-  the named workloads; synthetic small-dimension cases add two bf16 ulps of
-  each contributing term (check_block explains why); rows the oracle gives
+* end to end: max |d out| <= 2e-2 RMS(out_oracle) at every compared element,
+  in every case; each check records its ratio max |d out| / (2e-2 RMS)
+  (PARITY_RATIO_LOG names a file that collects them); rows the oracle gives
   exactly zero must be exactly zero.
 """
 
@@ -145,12 +145,14 @@ def compare_h(h_gpu, h_orc, what=""):
     apart (the GPU rounds an fp32 sum, the oracle an fp64 sum; measured ~0.1 %
     of values); silu then moves the SwiGLU value by up to a few percent for a
     large negative gate, where it is tiny. So: per element
-    |dh| <= 2^-6 |h| + 2^-10 RMS(h), and >= 98 % bit-identical among the values
-    with |h| >= 2^-24 RMS(h) (the rest are numerically zero next to the row)."""
+    |dh| <= 2^-6 |h| + 2^-10 RMS(h) + 2^-133 (one step of the bf16 subnormal
+    grid, where a relative bound says nothing), and >= 98 % bit-identical
+    among the values with |h| >= 2^-24 RMS(h) (the rest are numerically zero
+    next to the row)."""
     a, b = bf16_val(h_gpu), bf16_val(h_orc)
     rms = np.sqrt(np.mean(b * b))
     err = np.abs(a - b)
-    tol = 2.0**-6 * np.abs(b) + 2.0**-10 * rms
+    tol = 2.0**-6 * np.abs(b) + 2.0**-10 * rms + 2.0**-133
     bad = np.flatnonzero(err > tol)
     assert bad.size == 0, f"{what}: {bad.size} values off, e.g. [{bad[0]}] {a[bad[0]]} vs {b[bad[0]]}"
     sig = np.abs(b) >= 2.0**-24 * rms
@@ -161,12 +163,13 @@ def compare_h(h_gpu, h_orc, what=""):
 def compare_y_step(y_gpu, y_ref, h_gpu, w_dense, what=""):
     """Down GEMM on the same (GPU) SwiGLU row: the only differences are the fp32
     accumulation order and a bf16 rounding flip it can cause:
-    |dy| <= 2^-7 |y| + (K/32 + 64) 2^-24 sum_i |h_i w_ci|, >= 99 % identical."""
+    |dy| <= 2^-7 |y| + (K/32 + 64) 2^-24 sum_i |h_i w_ci| + 2^-133 (a step of
+    the subnormal grid), >= 99 % identical."""
     a, b = bf16_val(y_gpu), bf16_val(y_ref)
     hv = bf16_val(h_gpu)
     mag = np.abs(w_dense) @ np.abs(hv)
     K = hv.shape[0]
-    tol = 2.0**-7 * np.abs(b) + (K / 32 + 64) * 2.0**-24 * mag
+    tol = 2.0**-7 * np.abs(b) + (K / 32 + 64) * 2.0**-24 * mag + 2.0**-133
     err = np.abs(a - b)
     bad = np.flatnonzero(err > tol)
     assert bad.size == 0, f"{what}: {bad.size} values off, e.g. [{bad[0]}] {a[bad[0]]} vs {b[bad[0]]}"
@@ -176,23 +179,27 @@ def compare_y_step(y_gpu, y_ref, h_gpu, w_dense, what=""):
 
 def check_ffn_rows(inp, g, bk, rows_sel) -> dict:
     """Step-wise parity of the chosen bucket rows; returns the oracle's own
-    end-to-end y rows {row: y}."""
+    end-to-end y rows {row: y}. Rows are taken expert by expert, so that only
+    one expert's decoded down matrix is held at a time."""
     from tests._ref import decode_mx
 
     cfg = inp["cfg"]
     h_all, _ = gpu_h(g, cfg)
-    dense = {}
     y_o = {}
+    by_el: dict = {}
     for r in rows_sel:
         el = int(np.searchsorted(bk["offsets"], r, side="right") - 1)
-        t = int(bk["rows"][r])
-        _, h_o = oracle.mx_gate_up(inp["x"][t], inp["w13q"][el], inp["w13s"][el])
-        compare_h(h_all[r], h_o, f"h of bucket row {r} (expert {el}, token {t})")
-        if el not in dense:
-            dense[el] = decode_mx(inp["w2q"][el], inp["w2s"][el])
-        y_ref = oracle.mx_down(h_all[r], inp["w2q"][el], inp["w2s"][el])
-        compare_y_step(g["y"][r], y_ref, h_all[r], dense[el], f"y of bucket row {r}")
-        y_o[int(r)] = oracle.mx_down(h_o, inp["w2q"][el], inp["w2s"][el])
+        by_el.setdefault(el, []).append(int(r))
+    for el, rows in sorted(by_el.items()):
+        dense = decode_mx(inp["w2q"][el], inp["w2s"][el])
+        for r in rows:
+            t = int(bk["rows"][r])
+            _, h_o = oracle.mx_gate_up(inp["x"][t], inp["w13q"][el], inp["w13s"][el])
+            compare_h(h_all[r], h_o, f"h of bucket row {r} (expert {el}, token {t})")
+            y_ref = oracle.mx_down(h_all[r], inp["w2q"][el], inp["w2s"][el])
+            compare_y_step(g["y"][r], y_ref, h_all[r], dense, f"y of bucket row {r}")
+            y_o[r] = oracle.mx_down(h_o, inp["w2q"][el], inp["w2s"][el])
+        del dense
     return y_o
 
 
@@ -211,15 +218,30 @@ def check_shared_rows(inp, g, tokens) -> dict:
     return y_o
 
 
-def check_block(inp, g, tokens=None, strict=True) -> None:
-    """Everything, step by step, on all tokens or on ``tokens`` only.
+# max |d out| / (2e-2 RMS(out)) of every end-to-end check in this process,
+# as (test id, ratio, elements over the plain bound); PARITY_RATIO_LOG names a
+# file that each check also appends its line to
+RATIOS: list = []
 
-    End to end, ``strict`` applies the plain bound max |d out| <= 2e-2 RMS(out).
-    Otherwise (synthetic small-dimension cases) each element may also move by
-    two bf16 ulps of every term that reaches it, 2^-7 (sum_s w_s |z_s| + |y_sh|):
-    one legitimate rounding flip at a bf16 hand-off moves an expert output by an
-    ulp, and an element several times the output RMS then exceeds the plain
-    bound on its own."""
+
+def _record_ratio(ratio: float, n_over: int, note: str = "") -> None:
+    """Print and (PARITY_RATIO_LOG) append one check's end-to-end ratio."""
+    import os
+
+    case = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    RATIOS.append((case, ratio, n_over))
+    line = f"{case}\t{ratio:.4f}\t{n_over}\t{note}"
+    print(f"parity ratio: {line}")
+    path = os.environ.get("PARITY_RATIO_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
+def check_block(inp, g, tokens=None) -> float:
+    """Everything, step by step, on all tokens or on ``tokens`` only; returns
+    max |d out| / (2e-2 RMS(out)), records it, and requires it <= 1 (the
+    plain bound max |d out| <= 2e-2 RMS(out) at every element)."""
     cfg = inp["cfg"]
     lo = check_logits(inp, g)
     check_topk(inp, g, lo)
@@ -250,19 +272,16 @@ def check_block(inp, g, tokens=None, strict=True) -> None:
     got = g["out"][tokens].astype(np.float64)
     rms = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
     err = np.abs(got - ref)
-    bound = np.full_like(ref, 2e-2 * rms + 1e-30)
-    if not strict:
-        eps = float(np.float32(cfg.eps))
-        for i, t in enumerate(tokens):
-            for s_, p in enumerate(g["pick_pos"][t]):
-                if p >= 0:
-                    z = oracle.norm_row(y_o[p], inp.get("gamma"), eps)
-                    bound[i] += 2.0**-7 * abs(float(w_o[t, s_])) * np.abs(z)
-            if cfg.shared_I:
-                bound[i] += 2.0**-7 * np.abs(bf16_val(y_o[R + t]))
-    worst = np.unravel_index(np.argmax(err - bound), err.shape) if err.size else None
-    assert np.all(err <= bound), (
-        f"end to end: |d out| {err[worst]:.3g} > bound {bound[worst]:.3g} (2e-2 RMS = {2e-2 * rms:.3g})"
-    )
+    plain = 2e-2 * rms + 1e-30
+    ratio = float(err.max() / plain) if err.size else 0.0
+    over = err > plain
+    _record_ratio(ratio, int(over.sum()))
+    if over.any():
+        worst = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(
+            f"end to end: |d out| {err[worst]:.3g} > 2e-2 RMS = {plain:.3g} "
+            f"(token {tokens[worst[0]]}, column {worst[1]}; {int(over.sum())} elements over)"
+        )
     zero = np.all(ref == 0, axis=1)
     assert np.all(got[zero] == 0), "tokens without a local pick must be exactly zero"
+    return ratio

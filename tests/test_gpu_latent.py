@@ -14,7 +14,7 @@ Tolerances (tests/gpu_util.py derives the shared ones):
   different fp64 summation order of the squares) and >= 99.9 % identical;
 * the whole latent chain (pre -> norm -> top-k -> bucket -> experts ->
   combine -> post): ids exact, and the final rows within 2e-2 of their RMS
-  plus two bf16 ulps of each term, as check_block's non-strict bound.
+  (the ratio is recorded as check_block records its own).
 """
 
 import numpy as np
@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 from synth import PROJ_CONFIGS, ProjConfig, get_config, make_inputs, make_proj_inputs  # noqa: E402
 from tests._ref import bf16_val, nearest_bf16_bits  # noqa: E402
-from tests.gpu_util import compare_y_step, to_np  # noqa: E402
+from tests.gpu_util import _record_ratio, compare_y_step, to_np  # noqa: E402
 
 
 @pytest.fixture(autouse=True)
@@ -181,10 +181,9 @@ def test_latent_chain(bias_mode):
     ref = bf16_val(oracle.post_proj(part, pin["w_post"]))
     got = bf16_val(to_np(st.out))
     rms = np.sqrt(np.mean(ref * ref))
-    # a bf16 flip anywhere upstream moves a term by an ulp: two ulps of each
-    # output's magnitude on top of the plain bound
-    bound = 2e-2 * rms + 2.0**-7 * np.abs(ref)
-    assert np.all(np.abs(got - ref) <= bound), f"max error {np.abs(got - ref).max():.3g}, rms {rms:.3g}"
+    ratio = float(np.abs(got - ref).max() / (2e-2 * rms))
+    _record_ratio(ratio, int((np.abs(got - ref) > 2e-2 * rms).sum()))
+    assert ratio <= 1.0, f"max error {np.abs(got - ref).max():.3g}, rms {rms:.3g}"
 
 
 def _random_proj(seed):
