@@ -252,6 +252,30 @@ int moe_forward(const moe_dims* dims, const void* x, const float* w_router, cons
                 int32_t* pick_pos, int32_t* active, void* y, float* out, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc): moe_forward without a workspace
+ * argument. Its scratch is a static device array of MOE_STATIC_SCRATCH_BYTES
+ * in the library, one per GPU, held from the first call on that GPU until the
+ * process ends. The call allocates nothing and calls no allocating routine.
+ *   Arguments and outputs are moe_forward's, without workspace and
+ *   workspace_bytes; the device is the current one (that of `stream`).
+ *   wait_error: a device int32, or NULL: set to 0 at the start of the call
+ *   and nonzero if a wait in the expert-FFN launch hit its time bound (a
+ *   correct run never does; the outputs are then undefined).
+ * Returns moe_forward's codes; MOE_ERR_WORKSPACE when moe_forward_workspace_
+ * bytes(dims) exceeds MOE_STATIC_SCRATCH_BYTES (checked on the host before
+ * anything is enqueued). Every call on a GPU shares that GPU's array and
+ * clears its control words first: calls that overlap on one GPU (several
+ * streams, several host threads) race and must not be made. Outputs are
+ * bit-identical to moe_forward's for the same inputs. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int moe_forward_static(const moe_dims* dims, const void* x, const float* w_router,
+                       const float* bias, const void* w13_packed, const void* w2_packed,
+                       const void* ws13_packed, const void* ws2_packed, const void* gamma,
+                       float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* rows, int32_t* pick_pos, int32_t* active,
+                       void* y, float* out, int32_t* wait_error, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* around the block: the latent projections                                  */
 /* ------------------------------------------------------------------------ */

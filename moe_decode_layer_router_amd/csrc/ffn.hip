@@ -366,7 +366,7 @@ FfnLayout ffn_layout(const moe_dims& m) {
 
 int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2, const void* ws13,
                const void* ws2, const int32_t* counts, const int32_t* rows, void* y,
-               void* workspace, hipStream_t stream) {
+               void* workspace, hipStream_t stream, int32_t* error_word) {
   const FfnLayout l = ffn_layout(m);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   FfnArgs a{};
@@ -381,7 +381,7 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   a.hs = reinterpret_cast<uint16_t*>(ws + l.hs);
   a.prod = reinterpret_cast<int32_t*>(ws + l.prod);
   a.ready = reinterpret_cast<int32_t*>(ws + l.ready);
-  a.error = reinterpret_cast<int32_t*>(ws + l.error);
+  a.error = error_word ? error_word : reinterpret_cast<int32_t*>(ws + l.error);
   a.y = static_cast<uint16_t*>(y);
   a.S = m.S;
   a.d = m.d;

@@ -57,9 +57,10 @@ inline int max_work(const moe_dims& m) {
 
 FfnLayout ffn_layout(const moe_dims& m);
 
-// enqueue the expert FFNs (after argument checks)
+// enqueue the expert FFNs (after argument checks); error_word: where a wait
+// that hits its bound records it (NULL: the workspace's own error word)
 int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2, const void* ws13,
                const void* ws2, const int32_t* counts, const int32_t* rows, void* y,
-               void* workspace, hipStream_t stream);
+               void* workspace, hipStream_t stream, int32_t* error_word = nullptr);
 
 }  // namespace moeblk

@@ -19,11 +19,18 @@
 // a last-arriving one inside the router launch, through device-coherent
 // stores, a counter and device-coherent loads, measured slower than this
 // launch boundary: 13.9 us against 4.9 + 6.9 us on the S = 8 workload.)
+#include <mutex>
+
 #include "bucket_dev.h"
 #include "ffn_launch.h"
 #include "host.h"
 #include "launch.h"
 #include "route_dev.h"
+
+// The scratch of moe_forward_static, one copy a device for the life of the
+// process. In host code `scratch` names a host-side stand-in, not device
+// memory: the device address comes from hipGetSymbolAddress (below).
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace moeblk {
 namespace {
@@ -59,6 +66,89 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
                 active);
 }
 
+// zero n16 16-byte words at p, and *word if given (the control words of the
+// FFN launch and a caller's error word): a kernel, not hipMemsetAsync, so
+// that a captured graph replays it as a kernel node
+__global__ void clear_kernel(uint4* __restrict__ p, size_t n16, int32_t* __restrict__ word) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (word && blockIdx.x == 0 && threadIdx.x == 0) *word = 0;
+}
+
+// the device address of `scratch` on the current device, looked up once per
+// device with that device current
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return MOE_ERR_HIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
+// the block on one stream, after the argument checks; the workspace holds the
+// router's K parts (S > 32), then the FFN's layout
+int forward_enqueue(const moe_dims& m, const void* x, const float* w_router, const float* bias,
+                    const void* w13_packed, const void* w2_packed, const void* ws13_packed,
+                    const void* ws2_packed, const void* gamma, float* logits, int32_t* topk_ids,
+                    float* topk_w, int32_t* counts, int32_t* offsets, int32_t* rows,
+                    int32_t* pick_pos, int32_t* active, void* y, float* out, void* workspace,
+                    hipStream_t stream, int32_t* error_word) {
+  const size_t parts_bytes = router_parts_bytes(m);
+  float* parts = parts_bytes ? static_cast<float*>(workspace) : nullptr;
+  void* ffn_ws = static_cast<uint8_t*>(workspace) + parts_bytes;
+  launch_router_logits(m, x, w_router, bias, logits, stream, parts);
+  if (m.S <= kTopkThreads / kWave) {
+    hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits,
+                       select_bias(m, bias), topk_ids, topk_w, counts, offsets, rows, pick_pos,
+                       active, m.S, m.E, m.topk, m.renorm, m.n_local, m.local_base, r_max(m));
+  } else {  // a wave a token needs more waves than one workgroup holds
+    launch_topk(m, logits, bias, topk_ids, topk_w, stream, parts, logits);
+    launch_bucket(m, topk_ids, counts, offsets, rows, pick_pos, active, stream);
+  }
+  const int frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y,
+                             ffn_ws, stream, error_word);
+  if (frc) return frc;
+  launch_combine(m, y, topk_w, pick_pos, gamma, out, stream);
+  return launch_status();
+}
+
+int check_forward_args(const moe_dims* dims, const void* x, const float* w_router,
+                       const float* bias, const void* w13_packed, const void* w2_packed,
+                       const void* ws13_packed, const void* ws2_packed, const void* gamma,
+                       float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* rows, int32_t* pick_pos, int32_t* active,
+                       void* y, float* out) {
+  const int rc = check_dims(dims);
+  if (rc) return rc;
+  const moe_dims& m = *dims;
+  MOE_REQUIRE(x && w_router && w13_packed && w2_packed && logits && topk_ids && topk_w && counts &&
+                  offsets && rows && pick_pos && active && y && out,
+              MOE_ERR_NULL);
+  MOE_REQUIRE(m.shared_I == 0 || (ws13_packed && ws2_packed), MOE_ERR_NULL);
+  MOE_REQUIRE(aligned16(x) && aligned16(w_router) && (!bias || aligned16(bias)) &&
+                  aligned16(w13_packed) && aligned16(w2_packed) &&
+                  (!ws13_packed || aligned16(ws13_packed)) && (!ws2_packed || aligned16(ws2_packed)) &&
+                  (!gamma || aligned16(gamma)) && aligned16(logits) && aligned16(topk_ids) &&
+                  aligned16(topk_w) && aligned16(counts) && aligned16(offsets) && aligned16(rows) &&
+                  aligned16(pick_pos) && aligned16(active) && aligned16(y) && aligned16(out),
+              MOE_ERR_ALIGN);
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moeblk
 
@@ -78,38 +168,43 @@ extern "C" int moe_forward(const moe_dims* dims, const void* x, const float* w_r
                            int32_t* offsets, int32_t* rows, int32_t* pick_pos, int32_t* active,
                            void* y, float* out, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
-  const int rc = check_dims(dims);
+  const int rc = check_forward_args(dims, x, w_router, bias, w13_packed, w2_packed, ws13_packed,
+                                    ws2_packed, gamma, logits, topk_ids, topk_w, counts, offsets,
+                                    rows, pick_pos, active, y, out);
   if (rc) return rc;
-  const moe_dims& m = *dims;
-  MOE_REQUIRE(x && w_router && w13_packed && w2_packed && logits && topk_ids && topk_w && counts &&
-                  offsets && rows && pick_pos && active && y && out && workspace,
-              MOE_ERR_NULL);
-  MOE_REQUIRE(m.shared_I == 0 || (ws13_packed && ws2_packed), MOE_ERR_NULL);
-  MOE_REQUIRE(aligned16(x) && aligned16(w_router) && (!bias || aligned16(bias)) &&
-                  aligned16(w13_packed) && aligned16(w2_packed) &&
-                  (!ws13_packed || aligned16(ws13_packed)) && (!ws2_packed || aligned16(ws2_packed)) &&
-                  (!gamma || aligned16(gamma)) && aligned16(logits) && aligned16(topk_ids) &&
-                  aligned16(topk_w) && aligned16(counts) && aligned16(offsets) && aligned16(rows) &&
-                  aligned16(pick_pos) && aligned16(active) && aligned16(y) && aligned16(out) &&
-                  aligned16(workspace),
-              MOE_ERR_ALIGN);
+  MOE_REQUIRE(workspace, MOE_ERR_NULL);
+  MOE_REQUIRE(aligned16(workspace), MOE_ERR_ALIGN);
   MOE_REQUIRE(workspace_bytes >= moe_forward_workspace_bytes(dims), MOE_ERR_WORKSPACE);
+  return forward_enqueue(*dims, x, w_router, bias, w13_packed, w2_packed, ws13_packed, ws2_packed,
+                         gamma, logits, topk_ids, topk_w, counts, offsets, rows, pick_pos, active,
+                         y, out, workspace, stream, nullptr);
+}
 
-  const size_t parts_bytes = router_parts_bytes(m);
-  float* parts = parts_bytes ? static_cast<float*>(workspace) : nullptr;
-  void* ffn_ws = static_cast<uint8_t*>(workspace) + parts_bytes;
-  launch_router_logits(m, x, w_router, bias, logits, stream, parts);
-  if (m.S <= kTopkThreads / kWave) {
-    hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits,
-                       select_bias(m, bias), topk_ids, topk_w, counts, offsets, rows, pick_pos, active, m.S, m.E, m.topk, m.renorm,
-                       m.n_local, m.local_base, r_max(m));
-  } else {  // a wave a token needs more waves than one workgroup holds
-    launch_topk(m, logits, bias, topk_ids, topk_w, stream, parts, logits);
-    launch_bucket(m, topk_ids, counts, offsets, rows, pick_pos, active, stream);
-  }
-  const int frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y,
-                             ffn_ws, stream);
-  if (frc) return frc;
-  launch_combine(m, y, topk_w, pick_pos, gamma, out, stream);
-  return launch_status();
+extern "C" int moe_forward_static(const moe_dims* dims, const void* x, const float* w_router,
+                                  const float* bias, const void* w13_packed, const void* w2_packed,
+                                  const void* ws13_packed, const void* ws2_packed,
+                                  const void* gamma, float* logits, int32_t* topk_ids,
+                                  float* topk_w, int32_t* counts, int32_t* offsets, int32_t* rows,
+                                  int32_t* pick_pos, int32_t* active, void* y, float* out,
+                                  int32_t* wait_error, hipStream_t stream) {
+  const int rc = check_forward_args(dims, x, w_router, bias, w13_packed, w2_packed, ws13_packed,
+                                    ws2_packed, gamma, logits, topk_ids, topk_w, counts, offsets,
+                                    rows, pick_pos, active, y, out);
+  if (rc) return rc;
+  const size_t need = moe_forward_workspace_bytes(dims);
+  MOE_REQUIRE(need <= MOE_STATIC_SCRATCH_BYTES, MOE_ERR_WORKSPACE);
+  void* base = nullptr;
+  const int src = scratch_address(&base);
+  if (src) return src;
+  // the FFN's control words (counters, ready flags, error word) must start at
+  // zero; the rest of the layout is written before it is read
+  const moe_dims& m = *dims;
+  const size_t ctl = router_parts_bytes(m) + ffn_layout(m).prod;
+  const size_t n16 = (need - ctl) / 16;
+  const int blocks = static_cast<int>(n16 / 256 + 1 < 256 ? n16 / 256 + 1 : 256);
+  hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(static_cast<uint8_t*>(base) + ctl), n16, wait_error);
+  return forward_enqueue(m, x, w_router, bias, w13_packed, w2_packed, ws13_packed, ws2_packed, gamma,
+                         logits, topk_ids, topk_w, counts, offsets, rows, pick_pos, active, y, out,
+                         base, stream, wait_error);
 }
