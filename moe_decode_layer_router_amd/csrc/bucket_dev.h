@@ -33,49 +33,66 @@ __device__ __forceinline__ void bucket_mark(BucketLds& L, int el, int t) {
   atomicOr(&L.mask[el][t >> 5], 1u << (t & 31));
 }
 
+// a store that other workgroups of the same launch may read (kCoh: through to
+// the coherence point, sc1), and the matching load
+template <bool kCoh>
+__device__ __forceinline__ void st_i32(int32_t* p, int32_t v) {
+  if constexpr (kCoh) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool kCoh>
+__device__ __forceinline__ int32_t ld_i32(const int32_t* p) {  // one load: not batched
+  if constexpr (kCoh) return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
 // From the marks: counts, offsets, active (wave 0), then every pick's bucket
 // row (rows, pick_pos; rows past the last bucket row are -1 up to R_max).
-// A token's ids must be distinct.
+// A token's ids must be distinct (ids: global or LDS). The counts and the
+// bucket rows are stored first; then mid() runs (all threads), then the rest.
+// kCoh: counts and rows are read by other workgroups of the same launch once
+// mid() has published them (stored through to the coherence point); the rest
+// is read only after the launch.
+template <bool kCoh = false, class Mid = NoMid>
 __device__ __forceinline__ void bucket_finish(const int32_t* __restrict__ ids, int S, int topk,
                                               int n_loc, int local_base, int R_max, BucketLds& L,
                                               int32_t* counts, int32_t* offsets, int32_t* rows,
-                                              int32_t* pick_pos, int32_t* active) {
+                                              int32_t* pick_pos, int32_t* active, Mid mid = Mid{}) {
   const int tid = threadIdx.x;
   const int nth = blockDim.x;
   const int npick = S * topk;
   // wave 0, lane e: expert e's count, its bucket offset (wave prefix sum) and
   // its slot in the active list (ballot of the experts with picks)
+  int c = 0, incl = 0, nv = 0;
+  uint64_t act = 0;
+  const int e = tid;
   if (tid < kWave) {
-    const int e = tid;
-    int c = 0;
     if (e < n_loc) {
 #pragma unroll
       for (int w = 0; w < kMaskWords; ++w) c += __popc(L.mask[e][w]);
     }
-    int incl = c;
+    incl = c;
 #pragma unroll
     for (int m = 1; m < 32; m <<= 1) {
       const int o = __shfl_up(incl, m, kWave);
       if (e >= m) incl += o;
     }
-    const uint64_t act = __ballot(e < n_loc && c > 0);
-    const int nv = __popcll(act);
+    act = __ballot(e < n_loc && c > 0);
+    nv = __popcll(act);
     if (e < n_loc) {
       L.off[e] = incl - c;
-      counts[e] = c;
-      offsets[e] = incl - c;
-      if (c > 0) active[1 + __popcll(act & ((1ull << e) - 1ull))] = e;
-      if (e >= nv) active[1 + e] = -1;
+      st_i32<kCoh>(&counts[e], c);
     }
-    if (e == n_loc - 1) {
-      L.off[n_loc] = incl;
-      offsets[n_loc] = incl;
-    }
-    if (e == 0) active[0] = nv;
+    if (e == n_loc - 1) L.off[n_loc] = incl;
   }
   __syncthreads();
 
-  for (int p = tid; p < npick; p += nth) {
+  // bucket row of pick p, -1 if not local
+  auto pos_of = [&](int p) {
     const int el = ids[p] - local_base;
     const int t = p / topk;
     int pos = -1;
@@ -88,10 +105,24 @@ __device__ __forceinline__ void bucket_finish(const int32_t* __restrict__ ids, i
         else if (w == (t >> 5)) below += __popc(bits & ((1u << (t & 31)) - 1u));
       }
       pos = L.off[el] + below;
-      rows[pos] = t;
     }
-    pick_pos[p] = pos;
+    return pos;
+  };
+  for (int p = tid; p < npick; p += nth) {
+    const int pos = pos_of(p);
+    if (pos >= 0) st_i32<kCoh>(&rows[pos], p / topk);
   }
+  mid();
+  if (tid < kWave) {
+    if (e < n_loc) {
+      offsets[e] = incl - c;
+      if (c > 0) active[1 + __popcll(act & ((1ull << e) - 1ull))] = e;
+      if (e >= nv) active[1 + e] = -1;
+    }
+    if (e == n_loc - 1) offsets[n_loc] = incl;
+    if (e == 0) active[0] = nv;
+  }
+  for (int p = tid; p < npick; p += nth) pick_pos[p] = pos_of(p);
   for (int r = L.off[n_loc] + tid; r < R_max; r += nth) rows[r] = -1;
 }
 

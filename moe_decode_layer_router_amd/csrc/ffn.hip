@@ -25,9 +25,12 @@
 //
 // The host does not know the bucket sizes, so a grid covers the largest
 // possible number of items.
+#include "bucket_dev.h"
 #include "ffn_dev.h"
 #include "ffn_launch.h"
 #include "host.h"
+#include "launch.h"
+#include "route_dev.h"
 
 namespace moeblk {
 
@@ -77,6 +80,105 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
     __hip_atomic_store(&flags[i * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The routing front (moe_forward): workgroup b < S takes token b's top-k
+// (from the router's logits, or summing its K parts), stores the ids through
+// to the coherence point and counts itself; workgroup S waits for all S,
+// buckets the picks (outputs stored through), then sets the kReadyLines flag
+// lines. smem: at least sizeof(BucketLds) + 4 KiB.
+__device__ __forceinline__ void route_front(const FfnArgs& a, int b, uint8_t* smem) {
+  const RouteFront& f = a.rf;
+  if (b < a.S) {
+    if (f.parts) {
+      auto red = reinterpret_cast<float(*)[4][kWave]>(smem);
+      if (f.sel_bias)
+        topk_parts_token<true, true>(f.parts, f.KP, f.lbias, f.sel_bias, f.logits_out, f.ids, f.w,
+                                     a.S, f.E, f.topk, f.renorm, b, red);
+      else
+        topk_parts_token<false, true>(f.parts, f.KP, f.lbias, nullptr, f.logits_out, f.ids, f.w,
+                                      a.S, f.E, f.topk, f.renorm, b, red);
+    } else if (threadIdx.x < kWave) {
+      if (f.sel_bias)
+        topk_token<true, NoMark, true>(f.logits_in, f.sel_bias, f.ids, f.w, nullptr, f.E, f.topk,
+                                       f.renorm, b, NoMark{});
+      else
+        topk_token<false, NoMark, true>(f.logits_in, nullptr, f.ids, f.w, nullptr, f.E, f.topk,
+                                        f.renorm, b, NoMark{});
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(f.topk_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    const long long t0 = clock64();
+    while (__hip_atomic_load(f.topk_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.S) {
+      __builtin_amdgcn_s_sleep(2);
+      if (clock64() - t0 > kWaitCycles) {
+        __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __hip_atomic_store(f.topk_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  BucketLds& L = *reinterpret_cast<BucketLds*>(smem);
+  int32_t* ids_l = reinterpret_cast<int32_t*>(smem + sizeof(BucketLds));
+  bucket_clear(L);
+  __syncthreads();
+  // every token's ids into LDS, all loads in flight at once (coherent loads:
+  // the top-k workgroups stored them in this launch)
+  const int npick = a.S * f.topk;
+  constexpr int kPer = kMaxTokens * 8 / (kSplit * kWave);
+  const __amdgpu_buffer_rsrc_t ir =
+      __builtin_amdgcn_make_buffer_rsrc(f.ids, 0, 0x7fffffff, 0x00020000);
+  int32_t v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int p = min(i * kSplit * kWave + static_cast<int>(threadIdx.x), npick - 1);
+    v[i] = __builtin_amdgcn_raw_buffer_load_b32(ir, static_cast<uint32_t>(p) * 4u, 0, kCpolSc1);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int p = i * kSplit * kWave + threadIdx.x;
+    if (p < npick) {
+      ids_l[p] = v[i];
+      const int el = v[i] - f.local_base;
+      if (el >= 0 && el < a.n_loc) bucket_mark(L, el, p / f.topk);
+    }
+  }
+  __syncthreads();
+  // counts and bucket rows first, then the flags, then the outputs read only
+  // after the launch
+  auto publish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are done
+    __syncthreads();
+    for (int i = threadIdx.x; i < kReadyLines; i += blockDim.x)
+      __hip_atomic_store(&f.ready[i * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  bucket_finish<true>(ids_l, a.S, f.topk, a.n_loc, f.local_base, a.R_max, L,
+                      const_cast<int32_t*>(a.counts), f.offsets, const_cast<int32_t*>(a.rows),
+                      f.pick_pos, f.active, publish);
+}
+
+// A workgroup that needs the routing (j: its index among them) waits for its
+// flag line (the router launch before this one cleared the lines); the
+// bucket outputs are then read with coherent loads.
+__device__ __forceinline__ void wait_route(const FfnArgs& a, int j) {
+  if (threadIdx.x == 0) {
+    const int32_t* line = &a.rf.ready[(j % kReadyLines) * kCtlStride];
+    const long long t0 = clock64();
+    while (__hip_atomic_load(const_cast<int32_t*>(line), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) == 0) {
+      __builtin_amdgcn_s_sleep(4);
+      if (clock64() - t0 > kWaitCycles) {
+        __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // The single launch (no shared expert), items of 16 bucket rows at every S;
 // PG / PD: chunks in flight a wave in gate_up / down tasks. Forward progress:
 // every gate_up workgroup id is below every down workgroup id, and workgroups
@@ -104,7 +206,9 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
 #ifndef MOE_SINGLE_PL_LARGE_S
 #define MOE_SINGLE_PL_LARGE_S 2
 #endif
-template <int PG, int PD, int PL>
+// kFront: the routing front runs as the first a.front workgroups, and every
+// other workgroup waits for it.
+template <int PG, int PD, int PL, bool kFront>
 __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_kernel(FfnArgs a) {
   constexpr int TTG = 1;
   constexpr int kRed = static_cast<int>(sizeof(f32x4_t)) * kSplit * TTG * 4 * kWave;
@@ -112,11 +216,19 @@ __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_ker
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRed > kStage ? kRed : kStage];
   auto red = reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(smem);
   const int lane = threadIdx.x & (kWave - 1);
-  const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
+  int t = blockIdx.x;
+  if constexpr (kFront) {
+    if (t < a.front) {
+      route_front(a, t, smem);
+      return;
+    }
+    t -= a.front;
+    wait_route(a, t);
+  }
+  const int cnt = lane < a.n_loc ? ld_i32<kFront>(&a.counts[lane]) : 0;
   const int n_work = count_work<TTG>(cnt);
   const int RB13 = 2 * a.I / kRowsPerBlock, NC13 = a.d / kChunkK;
   const int RB2 = a.d / kRowsPerBlock, NC2 = a.I / kChunkK;
-  int t = blockIdx.x;
   int el, row0, ntok;
   if (t < n_work * RB13) {
     const int wi = t / RB13, rb = t - wi * RB13;
@@ -124,7 +236,8 @@ __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_ker
     const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB13 + rb) * NC13 * kMxTileBytes;
     const int32_t* rows = a.rows;
     ffn_task<true, TTG, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
-                                        [rows](int r) { return rows[r]; }, NoWait{}, red);
+                                        [rows](int r) { return ld_i32<kFront>(rows + r); },
+                                        NoWait{}, red);
     publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
     return;
   }
@@ -208,13 +321,25 @@ constexpr int pair_smem() {
 #ifndef MOE_SG_PW
 #define MOE_SG_PW 4  // weight chunks in flight a wave, shared gate_up tasks
 #endif
-template <int TTG, int P, bool kShared, int OCC = 2, int kLdsB = kPairLdsB, bool kSgRows = false>
+// kFront: the routing front runs as the first a.front workgroups; the routed
+// tasks wait for it (the shared expert's tasks do not need it).
+template <int TTG, int P, bool kShared, int OCC = 2, int kLdsB = kPairLdsB, bool kSgRows = false,
+          bool kFront = false>
 __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG, kLdsB>()];
   static_assert(!kSgRows || pair_smem<TTG, kLdsB>() >= kSdSmem, "LDS of the shared task");
+  static_assert(pair_smem<TTG, kLdsB>() >= sizeof(BucketLds) + 4 * kMaxTokens * 8,
+                "LDS of the routing front");
   auto red = reinterpret_cast<f32x4_t(*)[kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave]>(smem);
   const int NC = a.d / kChunkK;
   int t = blockIdx.x;
+  if constexpr (kFront) {
+    if (t < a.front) {
+      route_front(a, t, smem);
+      return;
+    }
+    t -= a.front;
+  }
   if constexpr (kShared) {
     constexpr int GS = 16 * kSharedTTG;
     const int RBs = 2 * a.Is / kRowsPerBlock;
@@ -236,10 +361,11 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a)
     }
     t -= n_sg * RBs;
   }
+  if constexpr (kFront) wait_route(a, t);
   const int RB = 2 * a.I / kRowsPerBlock;
   const int wi = t / RB, rb = t - wi * RB;
   const int lane = threadIdx.x & (kWave - 1);
-  const int cnt = lane < a.n_loc ? a.counts[lane] : 0;
+  const int cnt = lane < a.n_loc ? ld_i32<kFront>(&a.counts[lane]) : 0;
   int el, row0, ntok;
   if (!find_task<TTG>(cnt, wi, el, row0, ntok)) return;
   el = __builtin_amdgcn_readfirstlane(el);
@@ -247,20 +373,20 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a)
   ntok = __builtin_amdgcn_readfirstlane(ntok);
   const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
   const int32_t* rows = a.rows;
+  auto src_of = [rows](int r) { return ld_i32<kFront>(rows + r); };
   if (ntok <= 16 && ntok * a.d * 2 <= kLdsB) {
     ffn_task_ldsb<MOE_PAIR_LDSB_PG, 1, kLdsB, true, false>(
-        tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; }, NoWait{},
-        smem);
+        tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, src_of, NoWait{}, smem);
     return;
   }
   if (TTG > 1 && ntok <= 16) {  // one token tile: half the MFMAs and activation loads
     ffn_task<true, 1, MOE_PAIR_TT1_P, true, false>(
-        tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, [rows](int r) { return rows[r]; }, NoWait{},
+        tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, src_of, NoWait{},
         reinterpret_cast<f32x4_t(*)[1][4][kWave]>(smem));
     return;
   }
-  ffn_task<true, TTG, P, true, false>(tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I,
-                                      [rows](int r) { return rows[r]; }, NoWait{},
+  ffn_task<true, TTG, P, true, false>(tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, src_of,
+                                      NoWait{},
                                       reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(&red[0][0][0][0]));
 }
 
@@ -326,14 +452,22 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
 }
 
 // PG / PD: chunks in flight a wave in gate_up / down; kLean: the shared tasks
-// as shared_rows_task, the launches at MOE_GU_OCC / MOE_DOWN_OCC workgroups a CU
+// as shared_rows_task, the launches at MOE_GU_OCC / MOE_DOWN_OCC workgroups a
+// CU; a.front: the routing front ahead of the gate_up launch's tasks
 template <int TTG, int PG, int PD, bool kShared, bool kLean>
 void launch_pair(const FfnArgs& a, hipStream_t stream) {
   constexpr int GS = 16 * kSharedTTG;
   const int n_sg = kShared ? (a.S + GS - 1) / GS : 0;
-  const int g1 = n_sg * (2 * a.Is / kRowsPerBlock) + a.max_work * (2 * a.I / kRowsPerBlock);
+  const int g1 = a.front + n_sg * (2 * a.Is / kRowsPerBlock) + a.max_work * (2 * a.I / kRowsPerBlock);
   const int g2 = (n_sg + a.max_work) * (a.d / kRowsPerBlock);
-  if constexpr (kLean)
+  if (a.front) {
+    if constexpr (kLean)
+      hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared, MOE_GU_OCC, MOE_GU_LDSB, true, true>),
+                         dim3(g1), dim3(kSplit * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared, 2, kPairLdsB, false, true>), dim3(g1),
+                         dim3(kSplit * kWave), 0, stream, a);
+  } else if constexpr (kLean)
     hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared, MOE_GU_OCC, MOE_GU_LDSB, true>), dim3(g1),
                        dim3(kSplit * kWave), 0, stream, a);
   else
@@ -359,14 +493,20 @@ FfnLayout ffn_layout(const moe_dims& m) {
   l.hs = round_up(static_cast<size_t>(R) * m.I * 2, 256);
   l.prod = l.hs + round_up(static_cast<size_t>(m.S) * m.shared_I * 2, 256);
   l.ready = l.prod + static_cast<size_t>(l.max_work) * kCtlStride * 4;
-  l.error = l.ready + static_cast<size_t>(l.max_work) * (m.d / kRowsPerBlock) * kCtlStride * 4;
+  l.route = l.ready + static_cast<size_t>(l.max_work) * (m.d / kRowsPerBlock) * kCtlStride * 4;
+  l.error = l.route + static_cast<size_t>(1 + kReadyLines) * kCtlStride * 4;
   l.total = l.error + 256;
   return l;
 }
 
+int32_t* route_ready_flags(const moe_dims& m, void* workspace) {
+  return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + ffn_layout(m).route) +
+         kCtlStride;
+}
+
 int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2, const void* ws13,
                const void* ws2, const int32_t* counts, const int32_t* rows, void* y,
-               void* workspace, hipStream_t stream, int32_t* error_word) {
+               void* workspace, hipStream_t stream, int32_t* error_word, const FrontIo* front) {
   const FfnLayout l = ffn_layout(m);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   FfnArgs a{};
@@ -390,14 +530,44 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
   a.n_loc = m.n_local;
   a.R_max = r_max(m);
   a.max_work = l.max_work;
+  a.front = 0;
+  if (front) {  // the routing front: S top-k workgroups and the bucketing
+    RouteFront& f = a.rf;
+    f.logits_in = front->logits_in;
+    f.parts = front->parts;
+    f.KP = front->parts ? router_parts(m) : 0;
+    f.lbias = front->parts ? logit_bias(m, front->bias) : nullptr;
+    f.sel_bias = select_bias(m, front->bias);
+    f.logits_out = front->logits;
+    f.ids = front->ids;
+    f.w = front->w;
+    f.offsets = front->offsets;
+    f.pick_pos = front->pick_pos;
+    f.active = front->active;
+    f.topk_done = reinterpret_cast<int32_t*>(ws + l.route);  // reset by the bucketing
+    f.ready = reinterpret_cast<int32_t*>(ws + l.route) + kCtlStride;
+    f.E = m.E;
+    f.topk = m.topk;
+    f.renorm = m.renorm;
+    f.local_base = m.local_base;
+    a.front = m.S + 1;
+  }
   if (single_launch(m)) {
-    const int grid = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
-    if (m.S > 32)
-      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, MOE_SINGLE_PL_LARGE_S>), dim3(grid),
-                         dim3(kSplit * kWave), 0, stream, a);
+    const int tasks = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
+    const int grid = a.front + tasks;
+    if (a.front) {
+      if (m.S > 32)
+        hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, MOE_SINGLE_PL_LARGE_S, true>),
+                           dim3(grid), dim3(kSplit * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, 0, true>), dim3(grid),
+                           dim3(kSplit * kWave), 0, stream, a);
+    } else if (m.S > 32)
+      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, MOE_SINGLE_PL_LARGE_S, false>),
+                         dim3(grid), dim3(kSplit * kWave), 0, stream, a);
     else
-      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, 0>), dim3(grid), dim3(kSplit * kWave),
-                         0, stream, a);
+      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, 0, false>), dim3(grid),
+                         dim3(kSplit * kWave), 0, stream, a);
   } else if (ffn_group(m) > 16) {  // a shared expert, 32-row items
     launch_pair<2, MOE_PAIR_PG, MOE_PAIR_PD, true, true>(a, stream);
   } else {  // 16-row items: at MOE_DOWN_OCC a CU their ring of 4 chunks would spill

@@ -13,6 +13,30 @@ constexpr int kSharedTTG = 2;  // shared expert: 32-token groups
 #endif
 constexpr int kSharedP = MOE_SHARED_P;
 
+// The routing front of moe_forward's expert-FFN launch: the top-k of every
+// token (one workgroup a token) and the bucketing (one workgroup) run as the
+// launch's first workgroups, and the expert tasks wait for them on a flag
+// instead of a launch boundary (K3 page, stage "route": the routing is
+// computed inside the persistent launch that consumes it). counts and rows
+// are FfnArgs' (written here, read by the tasks).
+constexpr int kReadyLines = 64;  // copies of the routing-ready flag, one 128-byte line each
+struct RouteFront {
+  const float* logits_in;  // no K parts: the router's logits
+  const float* parts;      // else the router's K parts [KP][S][E]
+  int KP;
+  const float* lbias;      // K parts: the logit bias (added by the top-k), or NULL
+  const float* sel_bias;   // selection-only bias, or NULL
+  float* logits_out;       // K parts: the summed logits
+  int32_t* ids;
+  float* w;
+  int32_t* offsets;
+  int32_t* pick_pos;
+  int32_t* active;
+  int32_t* topk_done;      // workspace: tokens whose top-k is stored
+  int32_t* ready;          // workspace: kReadyLines flag lines
+  int E, topk, renorm, local_base;
+};
+
 struct FfnArgs {
   const uint8_t* w13;  // packed MXFP4 gate_up of the local experts
   const uint8_t* w2;   // packed MXFP4 down
@@ -28,16 +52,19 @@ struct FfnArgs {
   int32_t* ready;  // workspace: a flag a down task: its item's SwiGLU rows are written
   int32_t* error;  // workspace: nonzero if a wait hit its bound
   int S, d, I, Is, n_loc, R_max, max_work;
+  int front;       // workgroups of the routing front (S + 1), 0 without one
+  RouteFront rf;
 };
 
 // ints between two counters or flags (one 128-byte line each)
 constexpr int kCtlStride = 32;
 
 // workspace: SwiGLU rows h [R_max][I] and hs [S][Is] (bf16), then the
-// counters prod (max_work lines), the ready flags (max_work * d / 64 lines)
-// and the error word; these must start at zero and are left at zero
+// counters prod (max_work lines), the ready flags (max_work * d / 64 lines),
+// the routing front's counter and flags (1 + kReadyLines lines) and the error
+// word; these must start at zero and are left at zero
 struct FfnLayout {
-  size_t h, hs, prod, ready, error, total;
+  size_t h, hs, prod, ready, route, error, total;
   int max_work;
 };
 
@@ -57,10 +84,32 @@ inline int max_work(const moe_dims& m) {
 
 FfnLayout ffn_layout(const moe_dims& m);
 
+// The routing inputs and outputs of moe_forward's front (launch_ffn with a
+// front): the router's logits or K parts, the biases, and the outputs of
+// moe_route and moe_bucket.
+struct FrontIo {
+  const float* logits_in;
+  const float* parts;
+  const float* bias;  // the caller's bias (split by bias_mode)
+  float* logits;
+  int32_t* ids;
+  float* w;
+  int32_t* offsets;
+  int32_t* pick_pos;
+  int32_t* active;
+};
+
+// the routing-ready flags of the FFN launch's front: kReadyLines words
+// kCtlStride apart, which the router launch before it clears
+int32_t* route_ready_flags(const moe_dims& m, void* workspace);
+
 // enqueue the expert FFNs (after argument checks); error_word: where a wait
-// that hits its bound records it (NULL: the workspace's own error word)
+// that hits its bound records it (NULL: the workspace's own error word);
+// front: run the top-k and the bucketing as the launch's first workgroups
+// (counts and rows are then outputs)
 int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2, const void* ws13,
                const void* ws2, const int32_t* counts, const int32_t* rows, void* y,
-               void* workspace, hipStream_t stream, int32_t* error_word = nullptr);
+               void* workspace, hipStream_t stream, int32_t* error_word = nullptr,
+               const FrontIo* front = nullptr);
 
 }  // namespace moeblk

@@ -4,21 +4,16 @@
 //   1  router logits (S <= 16: one workgroup an expert row; S <= 32: 16
 //      tokens x a few rows a workgroup; beyond: tiles split over K, their
 //      parts in the workspace)
-//   2  top-k of every token and the bucketing, in one workgroup (S <= 16;
-//      beyond, one wave a token in its own launch -- for S > 32 one workgroup
-//      a token that first sums the router parts -- then the bucketing)
-//   3  the expert FFNs (ffn.hip: one launch, or two with a shared expert)
-//   4  per-pick RMSNorm and the weighted sum (one workgroup a token)
+//   2  the expert FFNs (ffn.hip: one launch, or two with a shared expert),
+//      whose first S + 1 workgroups take every token's top-k (summing the
+//      router's K parts beyond S = 32) and the bucketing; the expert tasks
+//      wait for them on flags in the workspace, the shared expert's tasks do
+//      not (K3 page, stage "route": the routing runs inside the persistent
+//      launch that consumes it)
+//   3  per-pick RMSNorm and the weighted sum (one workgroup a token)
 //
 // The outputs are those of moe_route, moe_bucket, moe_expert_ffn and
-// moe_combine, bit for bit: the same device code computes every value. For
-// S <= 16, step 2 replaces two launches of the four-call path. (Measured on MI355X: a
-// dependent launch costs about 2.5 us, while a grid-wide barrier inside one
-// launch costs tens of microseconds, so a chain of short launches is faster
-// than one persistent kernel. Handing the logits from the router workgroups to
-// a last-arriving one inside the router launch, through device-coherent
-// stores, a counter and device-coherent loads, measured slower than this
-// launch boundary: 13.9 us against 4.9 + 6.9 us on the S = 8 workload.)
+// moe_combine, bit for bit: the same device code computes every value.
 #include <mutex>
 
 #include "bucket_dev.h"
@@ -34,37 +29,6 @@ static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace moeblk {
 namespace {
-
-constexpr int kTopkThreads = 1024;
-
-// top-k of every token (wave w takes tokens w, w + 16, ...), marking the
-// local picks as they are found, then the bucketing (ids handed over in LDS),
-// in one workgroup
-__global__ __launch_bounds__(kTopkThreads) void topk_bucket_kernel(
-    const float* __restrict__ logits, const float* __restrict__ sel_bias,
-    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ rows,
-    int32_t* __restrict__ pick_pos, int32_t* __restrict__ active, int S, int E, int topk,
-    int renorm, int n_loc, int local_base, int R_max) {
-  __shared__ BucketLds L;
-  __shared__ int32_t ids_l[kMaxTokens * 8];
-  bucket_clear(L);
-  __syncthreads();
-  const int wv = threadIdx.x >> 6;
-  auto mark = [&](int id, int t) {
-    const int el = id - local_base;
-    if (el >= 0 && el < n_loc) bucket_mark(L, el, t);
-  };
-  if (sel_bias) {
-    for (int t = wv; t < S; t += kTopkThreads / kWave)
-      topk_token<true>(logits, sel_bias, ids, w, ids_l, E, topk, renorm, t, mark);
-  } else {
-    for (int t = wv; t < S; t += kTopkThreads / kWave)
-      topk_token<false>(logits, nullptr, ids, w, ids_l, E, topk, renorm, t, mark);
-  }
-  __syncthreads();
-  bucket_finish(ids_l, S, topk, n_loc, local_base, R_max, L, counts, offsets, rows, pick_pos,
-                active);
-}
 
 // zero n16 16-byte words at p, and *word if given (the control words of the
 // FFN launch and a caller's error word): a kernel, not hipMemsetAsync, so
@@ -110,17 +74,14 @@ int forward_enqueue(const moe_dims& m, const void* x, const float* w_router, con
   const size_t parts_bytes = router_parts_bytes(m);
   float* parts = parts_bytes ? static_cast<float*>(workspace) : nullptr;
   void* ffn_ws = static_cast<uint8_t*>(workspace) + parts_bytes;
-  launch_router_logits(m, x, w_router, bias, logits, stream, parts);
-  if (m.S <= kTopkThreads / kWave) {
-    hipLaunchKernelGGL(topk_bucket_kernel, dim3(1), dim3(kTopkThreads), 0, stream, logits,
-                       select_bias(m, bias), topk_ids, topk_w, counts, offsets, rows, pick_pos,
-                       active, m.S, m.E, m.topk, m.renorm, m.n_local, m.local_base, r_max(m));
-  } else {  // a wave a token needs more waves than one workgroup holds
-    launch_topk(m, logits, bias, topk_ids, topk_w, stream, parts, logits);
-    launch_bucket(m, topk_ids, counts, offsets, rows, pick_pos, active, stream);
-  }
+  // the router launch also clears the FFN launch's routing-ready flags
+  launch_router_logits(m, x, w_router, bias, logits, stream, parts, route_ready_flags(m, ffn_ws),
+                       kReadyLines, kCtlStride);
+  // the top-k and the bucketing run at the head of the expert-FFN launch
+  const FrontIo fio{parts ? nullptr : logits, parts, bias, logits, topk_ids, topk_w, offsets,
+                    pick_pos, active};
   const int frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y,
-                             ffn_ws, stream, error_word);
+                             ffn_ws, stream, error_word, &fio);
   if (frc) return frc;
   launch_combine(m, y, topk_w, pick_pos, gamma, out, stream);
   return launch_status();

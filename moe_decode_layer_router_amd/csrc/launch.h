@@ -56,8 +56,11 @@ inline size_t router_parts_bytes(const moe_dims& m) {
 // `parts` (router_parts_bytes of scratch) and S > kRouteSplitMinS the router
 // writes its K parts there and the top-k sums them into `logits_out`;
 // otherwise the router writes `logits` itself.
+// clear: n_clear words clear_stride apart that workgroup 0 sets to zero (the
+// routing-ready flags of moe_forward's FFN launch), or NULL
 void launch_router_logits(const moe_dims& m, const void* x, const float* wr, const float* bias,
-                          float* logits, hipStream_t stream, float* parts = nullptr);
+                          float* logits, hipStream_t stream, float* parts = nullptr,
+                          int32_t* clear = nullptr, int n_clear = 0, int clear_stride = 1);
 void launch_topk(const moe_dims& m, const float* logits, const float* bias, int32_t* ids, float* w,
                  hipStream_t stream, const float* parts = nullptr, float* logits_out = nullptr);
 void launch_bucket(const moe_dims& m, const int32_t* ids, int32_t* counts, int32_t* offsets,

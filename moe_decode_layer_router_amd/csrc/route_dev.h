@@ -304,7 +304,9 @@ __device__ __forceinline__ void order2(uint32_t& ka, int& ia, float& la, uint32_
 // mark(id, t) runs for each of the token's ids (lanes < topk).
 // topk_token_vals: the same with the token's logits already in registers
 // (lane l: lv[j] = logit of expert l + 64 j, any value for ids >= E).
-template <bool kSel, class Mark>
+// kCohIds: the ids are stored through to the coherence point (sc1), for
+// another workgroup of the same launch to read.
+template <bool kSel, class Mark, bool kCohIds = false>
 __device__ __forceinline__ void topk_token_vals(const float (&lv)[4],
                                                 const float* __restrict__ sel_bias,
                                                 int32_t* __restrict__ ids, float* __restrict__ w,
@@ -385,14 +387,18 @@ __device__ __forceinline__ void topk_token_vals(const float (&lv)[4],
   for (int q = 0; q < topk; ++q)
     sum += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sc), q));
   if (lane < topk) {
-    ids[static_cast<size_t>(t) * topk + lane] = my_id;
+    if constexpr (kCohIds)
+      __hip_atomic_store(&ids[static_cast<size_t>(t) * topk + lane], my_id, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else
+      ids[static_cast<size_t>(t) * topk + lane] = my_id;
     if (ids_lds) ids_lds[t * topk + lane] = my_id;
     mark(my_id, t);
     w[static_cast<size_t>(t) * topk + lane] = renorm ? sc / sum : sc;
   }
 }
 
-template <bool kSel, class Mark>
+template <bool kSel, class Mark, bool kCohIds = false>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
                                            const float* __restrict__ sel_bias,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
@@ -405,7 +411,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
     const int e = lane + kWave * j;
     lv[j] = e < E ? logits[static_cast<size_t>(t) * E + e] : 0.0f;
   }
-  topk_token_vals<kSel>(lv, sel_bias, ids, w, ids_lds, E, topk, renorm, t, mark);
+  topk_token_vals<kSel, Mark, kCohIds>(lv, sel_bias, ids, w, ids_lds, E, topk, renorm, t, mark);
 }
 
 // ---------------------------------------------------------------------------
@@ -556,8 +562,9 @@ __device__ __forceinline__ void router_split_tile(const uint16_t* __restrict__ x
 
 // Workgroup (4 waves, kWave * 4 threads): logits of token t = the sum of its
 // KP parts (wave w adds the parts w, w + 4, ... in order; then (0 + 1) +
-// (2 + 3)) + bias, written to logits[t]; then wave 0 takes its top-k.
-template <bool kSel>
+// (2 + 3)) + bias, written to logits[t]; then wave 0 takes its top-k
+// (kCohIds: as topk_token_vals).
+template <bool kSel, bool kCohIds = false>
 __device__ __forceinline__ void topk_parts_token(const float* __restrict__ parts, int KP,
                                                  const float* __restrict__ lbias,
                                                  const float* __restrict__ sel_bias,
@@ -600,7 +607,7 @@ __device__ __forceinline__ void topk_parts_token(const float* __restrict__ parts
       logits[static_cast<size_t>(t) * E + e] = lv[j];
     }
   }
-  topk_token_vals<kSel>(lv, sel_bias, ids, w, nullptr, E, topk, renorm, t, NoMark{});
+  topk_token_vals<kSel, NoMark, kCohIds>(lv, sel_bias, ids, w, nullptr, E, topk, renorm, t, NoMark{});
 }
 
 }  // namespace moeblk
