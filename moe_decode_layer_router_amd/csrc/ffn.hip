@@ -81,45 +81,52 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
 }
 
 // The routing front (moe_forward): workgroup b < S takes token b's top-k
-// (from the router's logits, or summing its K parts), stores the ids through
-// to the coherence point and counts itself; workgroup S waits for all S,
-// buckets the picks (outputs stored through), then sets the kReadyLines flag
-// lines. smem: at least sizeof(BucketLds) + 4 KiB.
+// (from the router's logits, or summing its K parts), sets the token's bit in
+// the mask of each local expert it picked, and, once its stores are done,
+// counts itself in every copy of the counter. Workgroup S waits for all S and
+// writes the bucket outputs (ids stored through by the top-k workgroups, read
+// back in one batch). smem: at least sizeof(BucketLds) + 4 KiB.
 __device__ __forceinline__ void route_front(const FfnArgs& a, int b, uint8_t* smem) {
   const RouteFront& f = a.rf;
   if (b < a.S) {
+    auto mark = [&](int id, int t) {
+      const int el = id - f.local_base;
+      if (el >= 0 && el < a.n_loc)
+        __hip_atomic_fetch_or(&f.masks[el * 4 + (t >> 5)], 1u << (t & 31), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    };
     if (f.parts) {
       auto red = reinterpret_cast<float(*)[4][kWave]>(smem);
       if (f.sel_bias)
         topk_parts_token<true, true>(f.parts, f.KP, f.lbias, f.sel_bias, f.logits_out, f.ids, f.w,
-                                     a.S, f.E, f.topk, f.renorm, b, red);
+                                     a.S, f.E, f.topk, f.renorm, b, red, mark);
       else
         topk_parts_token<false, true>(f.parts, f.KP, f.lbias, nullptr, f.logits_out, f.ids, f.w,
-                                      a.S, f.E, f.topk, f.renorm, b, red);
+                                      a.S, f.E, f.topk, f.renorm, b, red, mark);
     } else if (threadIdx.x < kWave) {
       if (f.sel_bias)
-        topk_token<true, NoMark, true>(f.logits_in, f.sel_bias, f.ids, f.w, nullptr, f.E, f.topk,
-                                       f.renorm, b, NoMark{});
+        topk_token<true, decltype(mark), true>(f.logits_in, f.sel_bias, f.ids, f.w, nullptr, f.E,
+                                               f.topk, f.renorm, b, mark);
       else
-        topk_token<false, NoMark, true>(f.logits_in, nullptr, f.ids, f.w, nullptr, f.E, f.topk,
-                                        f.renorm, b, NoMark{});
+        topk_token<false, decltype(mark), true>(f.logits_in, nullptr, f.ids, f.w, nullptr, f.E,
+                                                f.topk, f.renorm, b, mark);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are done
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores and atomics are done
     __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(f.topk_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < kDoneCopies)
+      __hip_atomic_fetch_add(&f.done[threadIdx.x * kCtlStride], 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   if (threadIdx.x == 0) {
     const long long t0 = clock64();
-    while (__hip_atomic_load(f.topk_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.S) {
-      __builtin_amdgcn_s_sleep(2);
+    while (__hip_atomic_load(f.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.S) {
+      __builtin_amdgcn_s_sleep(4);
       if (clock64() - t0 > kWaitCycles) {
         __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
-    __hip_atomic_store(f.topk_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   BucketLds& L = *reinterpret_cast<BucketLds*>(smem);
   int32_t* ids_l = reinterpret_cast<int32_t*>(smem + sizeof(BucketLds));
@@ -147,33 +154,62 @@ __device__ __forceinline__ void route_front(const FfnArgs& a, int b, uint8_t* sm
     }
   }
   __syncthreads();
-  // counts and bucket rows first, then the flags, then the outputs read only
-  // after the launch
-  auto publish = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are done
-    __syncthreads();
-    for (int i = threadIdx.x; i < kReadyLines; i += blockDim.x)
-      __hip_atomic_store(&f.ready[i * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  bucket_finish<true>(ids_l, a.S, f.topk, a.n_loc, f.local_base, a.R_max, L,
-                      const_cast<int32_t*>(a.counts), f.offsets, const_cast<int32_t*>(a.rows),
-                      f.pick_pos, f.active, publish);
+  bucket_finish(ids_l, a.S, f.topk, a.n_loc, f.local_base, a.R_max, L,
+                const_cast<int32_t*>(a.counts), f.offsets, const_cast<int32_t*>(a.rows),
+                f.pick_pos, f.active);
 }
 
 // A workgroup that needs the routing (j: its index among them) waits for its
-// flag line (the router launch before this one cleared the lines); the
-// bucket outputs are then read with coherent loads.
-__device__ __forceinline__ void wait_route(const FfnArgs& a, int j) {
+// copy of the counter to reach S; then each wave's lane e < n_loc loads local
+// expert e's token mask (coherent load) and returns its pick count.
+__device__ __forceinline__ int wait_route(const FfnArgs& a, int j, uint32_t (&mk)[4]) {
   if (threadIdx.x == 0) {
-    const int32_t* line = &a.rf.ready[(j % kReadyLines) * kCtlStride];
+    const int32_t* c = &a.rf.done[(j % kDoneCopies) * kCtlStride];
     const long long t0 = clock64();
-    while (__hip_atomic_load(const_cast<int32_t*>(line), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) == 0) {
+    while (__hip_atomic_load(const_cast<int32_t*>(c), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) < a.S) {
       __builtin_amdgcn_s_sleep(4);
       if (clock64() - t0 > kWaitCycles) {
         __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1);
+  const __amdgpu_buffer_rsrc_t mr =
+      __builtin_amdgcn_make_buffer_rsrc(a.rf.masks, 0, 0x7fffffff, 0x00020000);
+  const u32x4_t m = __builtin_amdgcn_raw_buffer_load_b128(
+      mr, static_cast<uint32_t>(min(lane, 31)) * 16u, 0, kCpolSc1);
+  int cnt = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mk[w] = lane < a.n_loc ? m[w] : 0u;
+    cnt += __popc(mk[w]);
+  }
+  return cnt;
+}
+
+// The tokens of bucket rows first .. first + ntok - 1 of local expert el (the
+// rank-th set bit of its mask is its bucket row offset + rank) into list[]:
+// wave 0 writes them, then the workgroup syncs. mk: the lanes' masks.
+__device__ __forceinline__ void front_rows(const uint32_t (&mk)[4], int el, int first, int ntok,
+                                           int32_t* list) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_readlane(mk[i], el);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = lane + kWave * h;  // tokens t and t + 64
+      const int wi = t >> 5;
+      const uint32_t below = w[wi] & ((1u << (t & 31)) - 1u);
+      int rank = __popc(below);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < wi) rank += __popc(w[i]);
+      if (((w[wi] >> (t & 31)) & 1u) && rank >= first && rank < first + ntok) list[rank - first] = t;
     }
   }
   __syncthreads();
@@ -217,27 +253,38 @@ __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_ker
   auto red = reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(smem);
   const int lane = threadIdx.x & (kWave - 1);
   int t = blockIdx.x;
+  uint32_t mk[4];
+  int cnt;
   if constexpr (kFront) {
     if (t < a.front) {
       route_front(a, t, smem);
       return;
     }
     t -= a.front;
-    wait_route(a, t);
+    cnt = wait_route(a, t, mk);
+  } else {
+    cnt = lane < a.n_loc ? a.counts[lane] : 0;
   }
-  const int cnt = lane < a.n_loc ? ld_i32<kFront>(&a.counts[lane]) : 0;
   const int n_work = count_work<TTG>(cnt);
   const int RB13 = 2 * a.I / kRowsPerBlock, NC13 = a.d / kChunkK;
   const int RB2 = a.d / kRowsPerBlock, NC2 = a.I / kChunkK;
   int el, row0, ntok;
   if (t < n_work * RB13) {
     const int wi = t / RB13, rb = t - wi * RB13;
-    find_task<TTG>(cnt, wi, el, row0, ntok);
+    int first;
+    find_task<TTG>(cnt, wi, el, row0, ntok, &first);
     const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB13 + rb) * NC13 * kMxTileBytes;
-    const int32_t* rows = a.rows;
-    ffn_task<true, TTG, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
-                                        [rows](int r) { return ld_i32<kFront>(rows + r); },
-                                        NoWait{}, red);
+    if constexpr (kFront) {  // the item's tokens from the masks, in LDS (read before red is)
+      int32_t* list = reinterpret_cast<int32_t*>(smem);
+      front_rows(mk, el, first, ntok, list);
+      ffn_task<true, TTG, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
+                                          [list, row0](int r) { return list[r - row0]; }, NoWait{},
+                                          red);
+    } else {
+      const int32_t* rows = a.rows;
+      ffn_task<true, TTG, PG, true, true>(tiles, NC13, a.x, a.d, row0, ntok, rb, a.h, a.I,
+                                          [rows](int r) { return rows[r]; }, NoWait{}, red);
+    }
     publish(&a.prod[wi * kCtlStride], RB13, &a.ready[wi * RB2 * kCtlStride], RB2);
     return;
   }
@@ -361,19 +408,26 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a)
     }
     t -= n_sg * RBs;
   }
-  if constexpr (kFront) wait_route(a, t);
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t mk[4];
+  int cnt;
+  if constexpr (kFront) cnt = wait_route(a, t, mk);
+  else cnt = lane < a.n_loc ? a.counts[lane] : 0;
   const int RB = 2 * a.I / kRowsPerBlock;
   const int wi = t / RB, rb = t - wi * RB;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int cnt = lane < a.n_loc ? ld_i32<kFront>(&a.counts[lane]) : 0;
-  int el, row0, ntok;
-  if (!find_task<TTG>(cnt, wi, el, row0, ntok)) return;
+  int el, row0, ntok, first;
+  if (!find_task<TTG>(cnt, wi, el, row0, ntok, &first)) return;
   el = __builtin_amdgcn_readfirstlane(el);
   row0 = __builtin_amdgcn_readfirstlane(row0);
   ntok = __builtin_amdgcn_readfirstlane(ntok);
+  first = __builtin_amdgcn_readfirstlane(first);
   const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB + rb) * NC * kMxTileBytes;
+  // the item's tokens: the bucket rows, or (front) from the masks into LDS,
+  // read before the task writes its LDS
+  int32_t* list = reinterpret_cast<int32_t*>(smem);
+  if constexpr (kFront) front_rows(mk, el, first, ntok, list);
   const int32_t* rows = a.rows;
-  auto src_of = [rows](int r) { return ld_i32<kFront>(rows + r); };
+  auto src_of = [rows, list, row0](int r) { return kFront ? list[r - row0] : rows[r]; };
   if (ntok <= 16 && ntok * a.d * 2 <= kLdsB) {
     ffn_task_ldsb<MOE_PAIR_LDSB_PG, 1, kLdsB, true, false>(
         tiles, NC, a.x, a.d, row0, ntok, rb, a.h, a.I, src_of, NoWait{}, smem);
@@ -494,14 +548,13 @@ FfnLayout ffn_layout(const moe_dims& m) {
   l.prod = l.hs + round_up(static_cast<size_t>(m.S) * m.shared_I * 2, 256);
   l.ready = l.prod + static_cast<size_t>(l.max_work) * kCtlStride * 4;
   l.route = l.ready + static_cast<size_t>(l.max_work) * (m.d / kRowsPerBlock) * kCtlStride * 4;
-  l.error = l.route + static_cast<size_t>(1 + kReadyLines) * kCtlStride * 4;
+  l.error = l.route + round_up(static_cast<size_t>(kFrontWords) * 4, 256);
   l.total = l.error + 256;
   return l;
 }
 
-int32_t* route_ready_flags(const moe_dims& m, void* workspace) {
-  return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + ffn_layout(m).route) +
-         kCtlStride;
+int32_t* route_front_block(const moe_dims& m, void* workspace) {
+  return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + ffn_layout(m).route);
 }
 
 int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2, const void* ws13,
@@ -544,8 +597,8 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
     f.offsets = front->offsets;
     f.pick_pos = front->pick_pos;
     f.active = front->active;
-    f.topk_done = reinterpret_cast<int32_t*>(ws + l.route);  // reset by the bucketing
-    f.ready = reinterpret_cast<int32_t*>(ws + l.route) + kCtlStride;
+    f.done = reinterpret_cast<int32_t*>(ws + l.route);
+    f.masks = reinterpret_cast<uint32_t*>(ws + l.route) + kDoneCopies * kCtlStride;
     f.E = m.E;
     f.topk = m.topk;
     f.renorm = m.renorm;

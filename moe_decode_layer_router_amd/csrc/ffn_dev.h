@@ -36,7 +36,8 @@ constexpr int kSplit = 4;  // waves a workgroup, = row tiles a task
 // bucket row (the bucket offsets are the exclusive prefix sums of the counts).
 // Returns false past the last item.
 template <int TTG>
-__device__ __forceinline__ bool find_task(int cnt, int wi, int& el, int& row0, int& ntok) {
+__device__ __forceinline__ bool find_task(int cnt, int wi, int& el, int& row0, int& ntok,
+                                          int* first = nullptr) {
   constexpr int G = 16 * TTG;
   const int lane = threadIdx.x & (kWave - 1);
   const int ng = (cnt + G - 1) / G;
@@ -58,6 +59,7 @@ __device__ __forceinline__ bool find_task(int cnt, int wi, int& el, int& row0, i
   el = u;
   row0 = __shfl(incl_cnt, u, kWave) - c + g * G;
   ntok = min(G, c - g * G);
+  if (first) *first = g * G;  // the item's first row within its expert's bucket
   return true;
 }
 

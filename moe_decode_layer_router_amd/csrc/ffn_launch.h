@@ -15,11 +15,19 @@ constexpr int kSharedP = MOE_SHARED_P;
 
 // The routing front of moe_forward's expert-FFN launch: the top-k of every
 // token (one workgroup a token) and the bucketing (one workgroup) run as the
-// launch's first workgroups, and the expert tasks wait for them on a flag
-// instead of a launch boundary (K3 page, stage "route": the routing is
-// computed inside the persistent launch that consumes it). counts and rows
-// are FfnArgs' (written here, read by the tasks).
-constexpr int kReadyLines = 64;  // copies of the routing-ready flag, one 128-byte line each
+// launch's first workgroups (K3 page, stage "route": the routing is computed
+// inside the persistent launch that consumes it). A top-k workgroup sets its
+// token's bit in the token mask of each local expert it picked and counts
+// itself; the expert tasks wait for the count to reach S and take their
+// expert counts and bucket rows from the masks (a bucket row's token is the
+// rank-th set bit of its expert's mask, as the bucketing numbers them), so
+// the bucketing, which writes the ABI's bucket outputs, is not on their path.
+// The counter (kDoneCopies copies, one 128-byte line each) and the masks are
+// cleared by the router launch before this one.
+constexpr int kDoneCopies = 8;
+constexpr int kMaskWordsAll = 32 * 4;  // 32 local experts x 128 tokens
+// words of the front's control block: the counter copies, then the masks
+constexpr int kFrontWords = kDoneCopies * 32 + kMaskWordsAll;
 struct RouteFront {
   const float* logits_in;  // no K parts: the router's logits
   const float* parts;      // else the router's K parts [KP][S][E]
@@ -32,8 +40,8 @@ struct RouteFront {
   int32_t* offsets;
   int32_t* pick_pos;
   int32_t* active;
-  int32_t* topk_done;      // workspace: tokens whose top-k is stored
-  int32_t* ready;          // workspace: kReadyLines flag lines
+  int32_t* done;           // workspace: kDoneCopies counters of finished top-k workgroups
+  uint32_t* masks;         // workspace: [32][4] token masks of the local experts
   int E, topk, renorm, local_base;
 };
 
@@ -61,8 +69,9 @@ constexpr int kCtlStride = 32;
 
 // workspace: SwiGLU rows h [R_max][I] and hs [S][Is] (bf16), then the
 // counters prod (max_work lines), the ready flags (max_work * d / 64 lines),
-// the routing front's counter and flags (1 + kReadyLines lines) and the error
-// word; these must start at zero and are left at zero
+// the routing front's control block (kFrontWords words) and the error word;
+// these must start at zero and are left at zero (the front's block is
+// cleared by moe_forward's router launch)
 struct FfnLayout {
   size_t h, hs, prod, ready, route, error, total;
   int max_work;
@@ -99,9 +108,9 @@ struct FrontIo {
   int32_t* active;
 };
 
-// the routing-ready flags of the FFN launch's front: kReadyLines words
-// kCtlStride apart, which the router launch before it clears
-int32_t* route_ready_flags(const moe_dims& m, void* workspace);
+// the control block of the FFN launch's front (kFrontWords words), which the
+// router launch before it clears
+int32_t* route_front_block(const moe_dims& m, void* workspace);
 
 // enqueue the expert FFNs (after argument checks); error_word: where a wait
 // that hits its bound records it (NULL: the workspace's own error word);

@@ -74,9 +74,9 @@ int forward_enqueue(const moe_dims& m, const void* x, const float* w_router, con
   const size_t parts_bytes = router_parts_bytes(m);
   float* parts = parts_bytes ? static_cast<float*>(workspace) : nullptr;
   void* ffn_ws = static_cast<uint8_t*>(workspace) + parts_bytes;
-  // the router launch also clears the FFN launch's routing-ready flags
-  launch_router_logits(m, x, w_router, bias, logits, stream, parts, route_ready_flags(m, ffn_ws),
-                       kReadyLines, kCtlStride);
+  // the router launch also clears the control block of the FFN launch's front
+  launch_router_logits(m, x, w_router, bias, logits, stream, parts, route_front_block(m, ffn_ws),
+                       kFrontWords, 1);
   // the top-k and the bucketing run at the head of the expert-FFN launch
   const FrontIo fio{parts ? nullptr : logits, parts, bias, logits, topk_ids, topk_w, offsets,
                     pick_pos, active};

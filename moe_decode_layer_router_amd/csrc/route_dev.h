@@ -563,15 +563,15 @@ __device__ __forceinline__ void router_split_tile(const uint16_t* __restrict__ x
 // Workgroup (4 waves, kWave * 4 threads): logits of token t = the sum of its
 // KP parts (wave w adds the parts w, w + 4, ... in order; then (0 + 1) +
 // (2 + 3)) + bias, written to logits[t]; then wave 0 takes its top-k
-// (kCohIds: as topk_token_vals).
-template <bool kSel, bool kCohIds = false>
+// (kCohIds, mark: as topk_token_vals).
+template <bool kSel, bool kCohIds = false, class Mark = NoMark>
 __device__ __forceinline__ void topk_parts_token(const float* __restrict__ parts, int KP,
                                                  const float* __restrict__ lbias,
                                                  const float* __restrict__ sel_bias,
                                                  float* __restrict__ logits,
                                                  int32_t* __restrict__ ids, float* __restrict__ w,
                                                  int S, int E, int topk, int renorm, int t,
-                                                 float (*red)[4][kWave]) {
+                                                 float (*red)[4][kWave], Mark mark = Mark{}) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
   // every load of the wave's parts in flight at once, then the adds in order
@@ -607,7 +607,7 @@ __device__ __forceinline__ void topk_parts_token(const float* __restrict__ parts
       logits[static_cast<size_t>(t) * E + e] = lv[j];
     }
   }
-  topk_token_vals<kSel, NoMark, kCohIds>(lv, sel_bias, ids, w, nullptr, E, topk, renorm, t, NoMark{});
+  topk_token_vals<kSel, Mark, kCohIds>(lv, sel_bias, ids, w, nullptr, E, topk, renorm, t, mark);
 }
 
 }  // namespace moeblk
