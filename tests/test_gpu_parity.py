@@ -88,7 +88,7 @@ EDGE = {
     "buckets_gt32": _tiny(S=64, E=8, n_local=8, topk=4),
     "buckets_gt48": _tiny(S=128, E=4, n_local=4, topk=3, d=512, I=256),
     "every_token_both": _tiny(S=128, E=2, n_local=2, topk=2, d=384, I=384),
-    "wide_and_narrow": _tiny(S=80, E=64, n_local=16, topk=4, bias_kind="zipf", zipf_s=1.5, d=1024),
+    "popular_expert_63": _tiny(S=80, E=64, n_local=16, topk=4, bias_kind="zipf", zipf_s=1.5, d=1024),
     "S128_buckets_gt64": _tiny(S=128, E=4, n_local=4, topk=2),
     "shared_small": _tiny(S=20, shared_I=128),
     "shared_S128": _tiny(S=128, E=16, n_local=4, topk=2, shared_I=256, d=256),
@@ -213,7 +213,7 @@ FUSED = {
     "buckets_gt32": _tiny(S=64, E=8, n_local=8, topk=4),
     "buckets_gt48": _tiny(S=128, E=4, n_local=4, topk=3, d=512, I=256),
     "every_token_both": _tiny(S=128, E=2, n_local=2, topk=2, d=384, I=384),
-    "wide_and_narrow": _tiny(S=80, E=64, n_local=16, topk=4, bias_kind="zipf", zipf_s=1.5, d=1024),
+    "popular_expert_63": _tiny(S=80, E=64, n_local=16, topk=4, bias_kind="zipf", zipf_s=1.5, d=1024),
     "shared_S128": _tiny(S=128, E=16, n_local=4, topk=2, shared_I=256, d=256),
     "d640_I256": _tiny(S=6, d=640, I=256, E=16, n_local=4, local_base=4, topk=3),
     "d7168_S33": _tiny(S=33, d=7168, I=128, E=32, n_local=8, topk=8),
