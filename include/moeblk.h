@@ -195,7 +195,9 @@ size_t moe_ffn_workspace_bytes(const moe_dims* dims);
  *              and the shared rows; other rows are left as they were;
  *   workspace  device scratch of at least moe_ffn_workspace_bytes(dims). It must
  *              be zero-filled once before its first use; every call leaves its
- *              counters at zero again (the rest is undefined afterwards).
+ *              counters at zero again (the rest is undefined afterwards). The
+ *              counters' place depends on the dims: a workspace used with
+ *              other dims must be zero-filled again.
  *              Calls sharing a workspace must not overlap. The 32-bit word at
  *              byte offset moe_ffn_workspace_bytes(dims) - 256 is set nonzero by
  *              a call in which a wait hit its time bound (a correct run never
@@ -238,13 +240,16 @@ int moe_combine(const moe_dims* dims, const void* y, const float* topk_w, const 
 size_t moe_forward_workspace_bytes(const moe_dims* dims);
 
 /* The whole block -- the work of moe_route, moe_bucket, moe_expert_ffn and
- * moe_combine -- on one stream. For S <= 16 top-k and bucketing share one
- * workgroup (one launch fewer than the four calls); beyond, the launches are
- * those of the four calls. Arguments and outputs are those of the four calls,
- * with identical values (the same device code computes every value). `workspace`
- * follows the moe_expert_ffn rules (zero-filled once before first use, error
- * word at byte moe_forward_workspace_bytes - 256, calls sharing it must not
- * overlap). */
+ * moe_combine -- on one stream (K3 page, stage "route": the routing is
+ * computed inside the launch that consumes it): the router launch, then the
+ * expert-FFN launch (two with a shared expert) whose first S + 1 workgroups
+ * take the top-k and the bucketing while its expert tasks wait for the
+ * routing, then the combine. Arguments and outputs are those of the four
+ * calls, with identical values (the same device code computes every value).
+ * `workspace` follows the moe_expert_ffn rules (zero-filled once before first
+ * use, error word at byte moe_forward_workspace_bytes - 256, calls sharing it
+ * must not overlap); a workspace used with other dims must be zero-filled
+ * again. */
 int moe_forward(const moe_dims* dims, const void* x, const float* w_router, const float* bias,
                 const void* w13_packed, const void* w2_packed, const void* ws13_packed,
                 const void* ws2_packed, const void* gamma, float* logits, int32_t* topk_ids,
