@@ -244,7 +244,9 @@ size_t moe_forward_workspace_bytes(const moe_dims* dims);
  * computed inside the launch that consumes it): the router launch, then the
  * expert-FFN launch (two with a shared expert) whose first S + 1 workgroups
  * take the top-k and the bucketing while its expert tasks wait for the
- * routing, then the combine. Arguments and outputs are those of the four
+ * routing, then the combine. Without a shared expert at S > 64 the top-k and
+ * the bucketing are launches of their own, as in the four calls (measured
+ * faster there). Arguments and outputs are those of the four
  * calls, with identical values (the same device code computes every value).
  * `workspace` follows the moe_expert_ffn rules (zero-filled once before first
  * use, error word at byte moe_forward_workspace_bytes - 256, calls sharing it

@@ -63,6 +63,13 @@ int scratch_address(void** out) {
   return MOE_OK;
 }
 
+// moe_forward runs the top-k and the bucketing as the routing front of the
+// expert-FFN launch with a shared expert (its tasks stream during the front)
+// or at S <= 64; without one at S > 64, where the front sums the router's K
+// parts for every token before any task starts, the separate top-k and
+// bucketing launches measured faster (S = 96 step: 86.2 against 84.7 us).
+bool routing_front(const moe_dims& m) { return m.shared_I > 0 || m.S <= 64; }
+
 // the block on one stream, after the argument checks; the workspace holds the
 // router's K parts (S > 32), then the FFN's layout
 int forward_enqueue(const moe_dims& m, const void* x, const float* w_router, const float* bias,
@@ -74,14 +81,23 @@ int forward_enqueue(const moe_dims& m, const void* x, const float* w_router, con
   const size_t parts_bytes = router_parts_bytes(m);
   float* parts = parts_bytes ? static_cast<float*>(workspace) : nullptr;
   void* ffn_ws = static_cast<uint8_t*>(workspace) + parts_bytes;
-  // the router launch also clears the control block of the FFN launch's front
-  launch_router_logits(m, x, w_router, bias, logits, stream, parts, route_front_block(m, ffn_ws),
-                       kFrontWords, 1);
-  // the top-k and the bucketing run at the head of the expert-FFN launch
-  const FrontIo fio{parts ? nullptr : logits, parts, bias, logits, topk_ids, topk_w, offsets,
-                    pick_pos, active};
-  const int frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y,
-                             ffn_ws, stream, error_word, &fio);
+  int frc;
+  if (routing_front(m)) {
+    // the router launch also clears the control block of the FFN launch's front
+    launch_router_logits(m, x, w_router, bias, logits, stream, parts,
+                         route_front_block(m, ffn_ws), kFrontWords, 1);
+    // the top-k and the bucketing run at the head of the expert-FFN launch
+    const FrontIo fio{parts ? nullptr : logits, parts, bias, logits, topk_ids, topk_w, offsets,
+                      pick_pos, active};
+    frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y, ffn_ws,
+                     stream, error_word, &fio);
+  } else {  // the four calls' launches
+    launch_router_logits(m, x, w_router, bias, logits, stream, parts);
+    launch_topk(m, logits, bias, topk_ids, topk_w, stream, parts, logits);
+    launch_bucket(m, topk_ids, counts, offsets, rows, pick_pos, active, stream);
+    frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y, ffn_ws,
+                     stream, error_word);
+  }
   if (frc) return frc;
   launch_combine(m, y, topk_w, pick_pos, gamma, out, stream);
   return launch_status();
