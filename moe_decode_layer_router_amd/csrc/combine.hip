@@ -11,8 +11,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const uint16_t* __restrict__ y, const float* __restrict__ tw, const int32_t* __restrict__ pick_pos,
     const uint16_t* __restrict__ gamma, float* __restrict__ out, int d, int topk, float eps,
     long shared_row0) {
-  __shared__ double red[8][kCombineThreads / kWave];
-  combine_token<VPT>(y, tw, pick_pos, gamma, out, d, topk, eps, shared_row0, blockIdx.x, red);
+  if constexpr (VPT <= 2) {  // d <= 8192: the picks' rows staged in LDS
+    __shared__ CombineLds L;
+    combine_token_staged<VPT>(y, tw, pick_pos, gamma, out, d, topk, eps, shared_row0, blockIdx.x, L);
+  } else {
+    __shared__ double red[8][kCombineThreads / kWave];
+    combine_token_slots<VPT>(y, tw, pick_pos, gamma, out, d, topk, eps, shared_row0, blockIdx.x,
+                             red);
+  }
 }
 
 template <int VPT>
