@@ -34,20 +34,24 @@ constexpr int kProjP = 2;  // chunks in flight a wave
 // tokens a task: 16 while S <= 16, else 32
 inline int proj_ttg(const moe_proj_dims& m) { return m.S > 16 ? 2 : 1; }
 
-// K parts: enough tasks to spread the weights over the chip, at least one
-// 128-K chunk a wave in every part
+// K parts: at least one 128-K chunk a wave in every part, and at most
+// max(128, 2 S) tasks. The task that completes a (row block, token group)
+// reads all of its parts, on one CU (about 28 GB/s), so more parts than that
+// cost more in the sum than they gain in the spread. Measured, us, at the
+// K5 page's shapes (pre: 512 rows, K = 8192 + 32 router rows; post: 1024
+// rows, K = 4096), tasks at most 2048 / 256 / 128: S = 128 pre 24.8 / 14.1 /
+// 16.4, post 17.8 / 13.4 / 15.0; S = 64 pre 13.9 / 13.9 / 10.7, post 12.9 /
+// 13.2 / 12.2; S <= 16 unchanged.
 #ifndef MOE_PROJ_MAX_PARTS
 #define MOE_PROJ_MAX_PARTS 16
-#endif
-#ifndef MOE_PROJ_MAX_TASKS
-#define MOE_PROJ_MAX_TASKS 2048
 #endif
 inline int proj_parts(const moe_proj_dims& m) {
   const int NC = m.K / kChunkK;
   const int G = 16 * proj_ttg(m);
   const int tasks = (m.N / kRowsPerBlock) * ((m.S + G - 1) / G);
+  const int max_tasks = m.S * 2 > 128 ? m.S * 2 : 128;
   for (int kp = MOE_PROJ_MAX_PARTS; kp > 1; kp >>= 1)
-    if (NC % kp == 0 && NC / kp >= kSplit && tasks * kp <= MOE_PROJ_MAX_TASKS) return kp;
+    if (NC % kp == 0 && NC / kp >= kSplit && tasks * kp <= max_tasks) return kp;
   return 1;
 }
 

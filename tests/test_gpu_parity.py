@@ -80,6 +80,7 @@ EDGE = {
     "S13_ragged": _tiny(S=13),
     "S37_k1": _tiny(S=37, topk=1),
     "k_eq_E": _tiny(S=5, E=4, n_local=4, topk=4),
+    "eight_local_picks": _tiny(S=12, E=8, n_local=8, topk=8, d=1024),
     "d384_I384": _tiny(S=9, d=384, I=384),
     "d640_I256": _tiny(S=6, d=640, I=256, E=16, n_local=4, local_base=4, topk=3),
     "n_local1": _tiny(S=16, E=8, n_local=1, local_base=3, topk=4),
