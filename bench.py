@@ -9,7 +9,8 @@ moe_combine. The headline workload is the largest of the row counts the
 metric spans: S = 128, d = 7168, 256 experts (32 local), I = 2048, top-8
 uniform routing, plus the always-on dense bf16 shared expert
 ("s128_shared"). The S = 8, 16 and 64 workloads ride along under
-``workloads`` (same protocol, fewer steps).
+``workloads`` (same protocol, fewer steps); at S = 8 and 16 they also time
+the block as one launch (moe_forward_one_launch, same outputs).
 
 Last-level-cache control: MI355X's 256 MB Infinity Cache would hold one
 step's active weights (about 94 MB here), so the benchmark keeps R copies of
@@ -262,6 +263,13 @@ def measure(cfg, K: int, warmup: int, copies_arg: int = 0, calib_copy_mib: int =
     st = per_call(blk.forward, K)
     # pass 4: the same weight copy every step (warm last-level cache, labelled)
     ms_warm = timed(lambda _i: blk.forward(0))
+    # pass 4b: the block as one launch, where moe_forward_one_launch takes it
+    # (S <= 16, d <= 4096, no shared expert): same outputs, timed beside
+    ms_one = None
+    if cfg.S <= 16 and cfg.d <= 4096 and not cfg.shared_I:
+        ms_one = timed(blk.forward_one_launch)
+        torch.cuda.synchronize()
+        assert blk.forward_error() == 0, "a wait in the one launch hit its bound"
     # pass 5: each expert-FFN call bracketed by events on its stream; routing
     # and buckets are those of the step (identical for every weight copy)
     blk.forward(0)
@@ -282,7 +290,7 @@ def measure(cfg, K: int, warmup: int, copies_arg: int = 0, calib_copy_mib: int =
     del blk
     torch.cuda.empty_cache()
     return dict(
-        inp=inp, ms=ms, ms4=ms4, st=st, ms_warm=ms_warm, ffn_ms=ffn_ms, b_ffn=b_ffn, b_mx=b_mx,
+        inp=inp, ms=ms, ms4=ms4, ms_one=ms_one, st=st, ms_warm=ms_warm, ffn_ms=ffn_ms, b_ffn=b_ffn, b_mx=b_mx,
         b_step_w=b_step_w, achieved=achieved, ffn_kernels=ffn_kernels, n_active=n_active,
         picks=picks, copies=copies,
     )
@@ -348,6 +356,7 @@ def main() -> int:
             "all_weight_pct_hbm_peak": round(100 * m["b_step_w"] / (m["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
             "mxfp4_weight_gbps": round(m["b_mx"] / (m["ms"] * 1e-3) / 1e9, 1),
             "four_call_ms_per_step": round(m["ms4"], 5),
+            "one_launch_ms_per_step": None if m["ms_one"] is None else round(m["ms_one"], 5),
             "active_local_experts": m["n_active"],
             "ffn_kernel": m["ffn_kernels"],
             "ffn_avg_ms": round(m["ffn_ms"], 5),

@@ -48,7 +48,8 @@
 extern "C" {
 #endif
 
-#define MOEBLK_ABI_VERSION 3 /* 2: moe_dims.bias_mode; 3: moe_route workspace */
+#define MOEBLK_ABI_VERSION 4 /* 2: moe_dims.bias_mode; 3: moe_route workspace;
+                                4: moe_forward_static, moe_forward_one_launch */
 
 /* status codes */
 #define MOE_OK 0
@@ -258,6 +259,32 @@ int moe_forward(const moe_dims* dims, const void* x, const float* w_router, cons
                 float* topk_w, int32_t* counts, int32_t* offsets, int32_t* rows,
                 int32_t* pick_pos, int32_t* active, void* y, float* out, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
+
+/* The whole block as ONE launch (Muse Spark K3 page, module docstring: the
+ * layer as one persistent launch; stage "route": the routing computed inside
+ * the launch that consumes it), for S <= 16, d <= 4096 and no shared expert.
+ * The launch's first E workgroups compute one router row each (summed as the
+ * router launch sums it), the next S + 1 take the top-k and the bucketing,
+ * then the expert tasks (gate_up hands its SwiGLU rows to down on flags),
+ * then one combine workgroup a token, which waits until its rows of y are
+ * written; every hand-off is a device-scope counter or flag in the
+ * workspace, and the last combine workgroup leaves them at zero for the next
+ * call. Measured on MI355X it is not faster than moe_forward's three
+ * launches (S = 8: about 2-3 us slower; S = 16: equal): each hand-off inside
+ * the launch costs about what the launch boundary it replaces did.
+ *   Arguments, outputs and workspace are moe_forward's (no shared expert:
+ *   no ws13/ws2), with identical values; the workspace rules are the same
+ *   (zero-filled once before first use; left ready for the next call with
+ *   the same dims, through either entry point; calls sharing it must not
+ *   overlap).
+ * Returns MOE_ERR_UNSUPPORTED outside S <= 16, d <= 4096, shared_I == 0,
+ * before anything is enqueued; otherwise moe_forward's codes. */
+int moe_forward_one_launch(const moe_dims* dims, const void* x, const float* w_router,
+                           const float* bias, const void* w13_packed, const void* w2_packed,
+                           const void* gamma, float* logits, int32_t* topk_ids, float* topk_w,
+                           int32_t* counts, int32_t* offsets, int32_t* rows, int32_t* pick_pos,
+                           int32_t* active, void* y, float* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate (code under HIP graph capture, serving
  * loops, harnesses that forbid hipMalloc): moe_forward without a workspace

@@ -35,6 +35,7 @@ __all__ = [
     "moe_forward_workspace_bytes",
     "moe_forward",
     "moe_forward_static",
+    "moe_forward_one_launch",
     "MOE_STATIC_SCRATCH_BYTES",
     "MoeProjDims",
     "proj_dims_from",
@@ -63,7 +64,7 @@ MOE_STATIC_SCRATCH_BYTES = 16 << 20  # moe_forward_static's static scratch a GPU
 
 
 # the layout of moe_dims and the entry points below (MOEBLK_ABI_VERSION)
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class MoeDims(ctypes.Structure):
@@ -145,6 +146,7 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_workspace_bytes.restype = ctypes.c_size_t
         L.moe_forward.argtypes = [_DP] + [_P] * 19 + [ctypes.c_size_t, _P]
         L.moe_forward_static.argtypes = [_DP] + [_P] * 19 + [_P]
+        L.moe_forward_one_launch.argtypes = [_DP] + [_P] * 17 + [ctypes.c_size_t, _P]
         _PD = ctypes.POINTER(MoeProjDims)
         L.moe_check_proj_dims.argtypes = [_PD]
         for f in ("moe_packed_dense_bytes", "moe_proj_workspace_bytes"):
@@ -157,7 +159,7 @@ def lib() -> ctypes.CDLL:
         L.moe_topk.argtypes = [_DP, _P, _P, _P, _P, _P]
         for f in (
             "moe_pack_mxfp4", "moe_pack_bf16", "moe_route", "moe_bucket", "moe_expert_ffn", "moe_combine",
-            "moe_forward", "moe_forward_static", "moe_check_proj_dims", "moe_pack_dense", "moe_pre_expert", "moe_latent_norm",
+            "moe_forward", "moe_forward_static", "moe_forward_one_launch", "moe_check_proj_dims", "moe_pack_dense", "moe_pre_expert", "moe_latent_norm",
             "moe_post_expert", "moe_topk",
         ):
             getattr(L, f).restype = ctypes.c_int
@@ -295,6 +297,20 @@ def moe_forward(dims, x, w_router, bias, w13_packed, w2_packed, ws13_packed, ws2
         "moe_forward", ctypes.byref(_d(dims)), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13_packed),
         _ptr(w2_packed), _ptr(ws13_packed), _ptr(ws2_packed), _ptr(gamma), _ptr(logits), _ptr(topk_ids),
         _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(rows), _ptr(pick_pos), _ptr(active), _ptr(y), _ptr(out),
+        _ptr(workspace), int(workspace_bytes), _stream(stream),
+    )
+
+
+def moe_forward_one_launch(dims, x, w_router, bias, w13_packed, w2_packed, gamma, logits, topk_ids, topk_w,
+                           counts, offsets, rows, pick_pos, active, y, out, workspace, workspace_bytes=None,
+                           stream=None) -> None:
+    """moe_forward as one launch (S <= 16, d <= 4096, no shared expert)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _call(
+        "moe_forward_one_launch", ctypes.byref(_d(dims)), _ptr(x), _ptr(w_router), _ptr(bias),
+        _ptr(w13_packed), _ptr(w2_packed), _ptr(gamma), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+        _ptr(counts), _ptr(offsets), _ptr(rows), _ptr(pick_pos), _ptr(active), _ptr(y), _ptr(out),
         _ptr(workspace), int(workspace_bytes), _stream(stream),
     )
 

@@ -21,6 +21,7 @@ from . import (
     moe_expert_ffn,
     moe_ffn_workspace_bytes,
     moe_forward,
+    moe_forward_one_launch,
     moe_forward_workspace_bytes,
     moe_pack_bf16,
     moe_pack_mxfp4,
@@ -140,6 +141,16 @@ class MoeBlock:
             self.dims, self.x, st["wr"], st["bias"], st["w13"], st["w2"], st["ws13"], st["ws2"], self.gamma,
             self.logits, self.ids, self.w, self.counts, self.offsets, self.rows, self.pick_pos, self.active,
             self.y, self.out, self.fws,
+        )
+
+    def forward_one_launch(self, s=0):
+        """The block through moe_forward_one_launch (S <= 16, d <= 4096, no
+        shared expert; same outputs as forward)."""
+        st = self.sets[s]
+        moe_forward_one_launch(
+            self.dims, self.x, st["wr"], st["bias"], st["w13"], st["w2"], self.gamma, self.logits,
+            self.ids, self.w, self.counts, self.offsets, self.rows, self.pick_pos, self.active, self.y,
+            self.out, self.fws,
         )
 
     @staticmethod

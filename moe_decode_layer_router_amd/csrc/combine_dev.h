@@ -298,38 +298,50 @@ __device__ __forceinline__ void combine_token_slots(const uint16_t* __restrict__
   }
 }
 
-// local picks of a token staged at once (one wave each), and the LDS of a
-// combine workgroup: kStagedPicks rows of up to kMaxStagedVec vectors of 8 bf16
+// local picks of a token staged at once (two waves each), and the LDS of a
+// combine workgroup: kStagedPicks rows of up to MV vectors of 8 bf16
 constexpr int kStagedPicks = 4;
 constexpr int kMaxStagedVec = 1024;  // d <= 8192
-struct CombineLds {
-  u32x4_t row[kStagedPicks][kMaxStagedVec];
+template <int MV>
+struct CombineLdsT {
+  u32x4_t row[kStagedPicks][MV];
   double ss[kStagedPicks][2];  // the two halves' sums of squares
 };
+using CombineLds = CombineLdsT<kMaxStagedVec>;
 
-// token t: out[t] = sum over slots s with pick_pos >= 0 of
-//   w[t][s] * y[p] / sqrt(mean(y[p]^2) + eps) * gamma  (+ y[shared_row0 + t]).
-// The token's local picks are taken in slot order, kStagedPicks at a time:
-// waves 2k and 2k + 1 load pick k's row once into LDS, each half of its
-// vectors (wave 2k + h: vectors 64 (2i + h) + lane), and sum its squares in
-// fp64 (a lane's vectors into 4 sums by i mod 4, added as (0 + 1) + (2 + 3),
-// then the wave's butterfly, then half 0 + half 1), so that all of the picks
-// cost one round trip; r = 1 / sqrt(ss / d + eps). Then every thread adds
-// the normalised rows in slot order from LDS, VPT vectors of 8 a thread, and
-// the shared expert's row last. A token's workgroup runs on one CU, whose
-// loads stream at about 28 GB/s: a token moves (picks + 1) rows of d bf16 and
-// its d fp32 outputs, the bound of the launch at S = 128. kCoh: the y rows were
-// written in the same launch by other workgroups (sc1 loads). d <= 8192.
-template <int VPT, bool kCoh = false>
+// token t: out[t] = sum over slots s with pick_pos[s] >= 0 of
+//   tw[s] * y[p] / sqrt(mean(y[p]^2) + eps) * gamma  (+ y[shared_row0 + t]),
+// pick_pos and tw: the token's topk slots. The token's local picks are taken
+// in slot order, kStagedPicks at a time: waves 2k and 2k + 1 load pick k's
+// row once into LDS, each half of its vectors (wave 2k + h: vectors
+// 64 (2i + h) + lane), and sum its squares in fp64 (a lane's vectors into 4
+// sums by i mod 4, added as (0 + 1) + (2 + 3), then the wave's butterfly,
+// then half 0 + half 1), so that all of the picks cost one round trip;
+// r = 1 / sqrt(ss / d + eps). Then every thread adds the normalised rows in
+// slot order from LDS, VPT vectors of 8 a thread, and the shared expert's row
+// last. Those are the 8 waves of kCombineThreads threads; a workgroup of NT
+// threads runs its wave w as waves w, w + NT / 64, ... and each thread takes
+// VPT * kCombineThreads / NT vectors, so that every value is summed in the
+// same order either way. A token's workgroup runs on one CU, whose loads
+// stream at about 28 GB/s: a token moves (picks + 1) rows of d bf16 and its
+// d fp32 outputs, the bound of the launch at S = 128. kCoh: the y rows were
+// written in the same launch by other workgroups (sc1 loads).
+// d <= 8 * VPT * kCombineThreads <= 8 * MV.
+template <int VPT, bool kCoh = false, int NT = kCombineThreads, int MV = kMaxStagedVec>
 __device__ __forceinline__ void combine_token_staged(const uint16_t* __restrict__ y,
                                                      const float* __restrict__ tw,
                                                      const int32_t* __restrict__ pick_pos,
                                                      const uint16_t* __restrict__ gamma,
                                                      float* __restrict__ out, int d, int topk,
                                                      float eps, long shared_row0, int t,
-                                                     CombineLds& L) {
-  static_assert(kCombineThreads / kWave == 2 * kStagedPicks, "two waves a staged pick");
-  static_assert(VPT * kCombineThreads <= kMaxStagedVec, "rows staged in LDS");
+                                                     CombineLdsT<MV>& L) {
+  constexpr int kVw = 2 * kStagedPicks;  // waves of the arithmetic
+  static_assert(kCombineThreads / kWave == kVw, "two waves a staged pick");
+  constexpr int PW = NT / kWave;         // waves of this workgroup
+  static_assert(kVw % PW == 0, "each wave runs whole waves of the arithmetic");
+  constexpr int kRuns = kVw / PW;
+  constexpr int VT = VPT * kCombineThreads / NT;  // vectors a thread
+  static_assert(VPT * kCombineThreads <= MV, "rows staged in LDS");
   const int nvec = d / 8;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const __amdgpu_buffer_rsrc_t yr =
@@ -339,8 +351,8 @@ __device__ __forceinline__ void combine_token_staged(const uint16_t* __restrict_
   float lw[8] = {};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const int p = s < topk ? pick_pos[static_cast<size_t>(t) * topk + s] : -1;
-    const float wv = s < topk ? tw[static_cast<size_t>(t) * topk + s] : 0.0f;
+    const int p = s < topk ? pick_pos[s] : -1;
+    const float wv = s < topk ? tw[s] : 0.0f;
 #pragma unroll
     for (int b = 0; b <= s; ++b) {
       if (p >= 0 && b == nl) {
@@ -352,18 +364,18 @@ __device__ __forceinline__ void combine_token_staged(const uint16_t* __restrict_
   }
   // the shared expert's row is loaded now, so that it arrives while the
   // routed picks are summed
-  u32x4_t shq[VPT];
+  u32x4_t shq[VT];
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int v = threadIdx.x + kCombineThreads * i;
+  for (int i = 0; i < VT; ++i) {
+    const int v = threadIdx.x + NT * i;
     shq[i] = u32x4_t{0u, 0u, 0u, 0u};
     if (shared_row0 >= 0 && v < nvec)
       shq[i] = load_y8<kCoh>(y, yr, static_cast<size_t>(shared_row0 + t) * d + 8 * v);
   }
-  float acc[VPT][8], gam[VPT][8];
+  float acc[VT][8], gam[VT][8];
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int v = threadIdx.x + kCombineThreads * i;
+  for (int i = 0; i < VT; ++i) {
+    const int v = threadIdx.x + NT * i;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       acc[i][j] = 0.0f;
@@ -380,37 +392,46 @@ __device__ __forceinline__ void combine_token_staged(const uint16_t* __restrict_
     }
   }
   constexpr int kPerLane = VPT * kCombineThreads / kWave / 2;  // a half row's vectors a lane
-  const int pk = w >> 1, half = w & 1;
 #pragma unroll
   for (int b0 = 0; b0 < 8; b0 += kStagedPicks) {
     if (b0 >= nl) break;  // uniform
     // waves 2k, 2k + 1: pick b0 + k into LDS, and its sum of squares
-    int p = 0;
+    u32x4_t q[kRuns][kPerLane];
 #pragma unroll
-    for (int k = 0; k < kStagedPicks; ++k)
-      if (pk == k) p = lp[b0 + k];
-    if (b0 + pk < nl) {
-      u32x4_t q[kPerLane];
+    for (int m = 0; m < kRuns; ++m) {
+      const int vw = w + PW * m, pk = vw >> 1, half = vw & 1;
+      int p = 0;
 #pragma unroll
-      for (int i = 0; i < kPerLane; ++i) {
-        const int v = min(kWave * (2 * i + half) + lane, nvec - 1);
-        q[i] = load_y8<kCoh>(y, yr, static_cast<size_t>(p) * d + 8 * v);
-      }
-      double ss4[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int k = 0; k < kStagedPicks; ++k)
+        if (pk == k) p = lp[b0 + k];
+      if (b0 + pk < nl) {
 #pragma unroll
-      for (int i = 0; i < kPerLane; ++i) {
-        const int v = kWave * (2 * i + half) + lane;
-        if (v >= nvec) continue;
-        L.row[pk][v] = q[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const double lo = bf16_lo(q[i][j]), hi = bf16_hi(q[i][j]);
-          ss4[i % 4] += lo * lo;
-          ss4[i % 4] += hi * hi;
+        for (int i = 0; i < kPerLane; ++i) {
+          const int v = min(kWave * (2 * i + half) + lane, nvec - 1);
+          q[m][i] = load_y8<kCoh>(y, yr, static_cast<size_t>(p) * d + 8 * v);
         }
       }
-      const double ss = wave_sum_f64((ss4[0] + ss4[1]) + (ss4[2] + ss4[3]));
-      if (lane == 0) L.ss[pk][half] = ss;
+    }
+#pragma unroll
+    for (int m = 0; m < kRuns; ++m) {
+      const int vw = w + PW * m, pk = vw >> 1, half = vw & 1;
+      if (b0 + pk < nl) {
+        double ss4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+          const int v = kWave * (2 * i + half) + lane;
+          if (v >= nvec) continue;
+          L.row[pk][v] = q[m][i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const double lo = bf16_lo(q[m][i][j]), hi = bf16_hi(q[m][i][j]);
+            ss4[i % 4] += lo * lo;
+            ss4[i % 4] += hi * hi;
+          }
+        }
+        const double ss = wave_sum_f64((ss4[0] + ss4[1]) + (ss4[2] + ss4[3]));
+        if (lane == 0) L.ss[pk][half] = ss;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -423,8 +444,8 @@ __device__ __forceinline__ void combine_token_staged(const uint16_t* __restrict_
       for (int b = 0; b < 8; ++b)
         if (b == b0 + k) wt = lw[b];
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int v = threadIdx.x + kCombineThreads * i;
+      for (int i = 0; i < VT; ++i) {
+        const int v = threadIdx.x + NT * i;
         if (v >= nvec) continue;
         const u32x4_t q = L.row[k][v];
 #pragma unroll
@@ -437,8 +458,8 @@ __device__ __forceinline__ void combine_token_staged(const uint16_t* __restrict_
     __syncthreads();  // the staged rows are read before the next picks overwrite them
   }
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int v = threadIdx.x + kCombineThreads * i;
+  for (int i = 0; i < VT; ++i) {
+    const int v = threadIdx.x + NT * i;
     if (v >= nvec) continue;
     if (shared_row0 >= 0) {
 #pragma unroll

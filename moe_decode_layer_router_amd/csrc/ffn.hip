@@ -26,6 +26,7 @@
 // The host does not know the bucket sizes, so a grid covers the largest
 // possible number of items.
 #include "bucket_dev.h"
+#include "combine_dev.h"
 #include "ffn_dev.h"
 #include "ffn_launch.h"
 #include "host.h"
@@ -80,14 +81,40 @@ __device__ __forceinline__ void publish(int32_t* ctr, int n, int32_t* flags, int
     __hip_atomic_store(&flags[i * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The routing front (moe_forward): workgroup b < S takes token b's top-k
-// (from the router's logits, or summing its K parts), sets the token's bit in
-// the mask of each local expert it picked, and, once its stores are done,
-// counts itself in every copy of the counter. Workgroup S waits for all S and
+// a workgroup that has read the routing counts itself on a seen line (one
+// launch: the control block is cleared once every reader has)
+__device__ __forceinline__ void count_seen(const FfnArgs& a) {
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(&a.rf.seen[(blockIdx.x % kSeenLines) * kCtlStride], 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The routing front (moe_forward). With router rows (RNW > 0), workgroup
+// b < E first computes expert row b's logits for every token (stored
+// through) and counts itself on its router line; the rest of the front
+// follows with b - E. Workgroup b < S takes token b's top-k (from the
+// router's logits, or summing its K parts), sets the token's bit in the mask
+// of each local expert it picked, and, once its stores are done, counts
+// itself in every copy of the counter. Workgroup S waits for all S and
 // writes the bucket outputs (ids stored through by the top-k workgroups, read
-// back in one batch). smem: at least sizeof(BucketLds) + 4 KiB.
+// back in one batch). smem: at least sizeof(BucketLds) + 4 KiB. kOne: the
+// whole block is one launch (the bucketing counts itself as a reader).
+template <int RNW, bool kOne>
 __device__ __forceinline__ void route_front(const FfnArgs& a, int b, uint8_t* smem) {
   const RouteFront& f = a.rf;
+  if constexpr (RNW > 0) {
+    if (b < f.n_router) {
+      router_row_w4<RNW, 4 / RNW>(a.x, f.wr, f.lbias, f.logits_out, a.S, a.d, f.E, b,
+                                  reinterpret_cast<float(*)[kRouteWaves][kTok]>(smem));
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's logit stores are done
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(&f.rdone[(b % kRouterLines) * kCtlStride], 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    b -= f.n_router;
+  }
   if (b < a.S) {
     auto mark = [&](int id, int t) {
       const int el = id - f.local_base;
@@ -103,6 +130,39 @@ __device__ __forceinline__ void route_front(const FfnArgs& a, int b, uint8_t* sm
       else
         topk_parts_token<false, true>(f.parts, f.KP, f.lbias, nullptr, f.logits_out, f.ids, f.w,
                                       a.S, f.E, f.topk, f.renorm, b, red, mark);
+    } else if (RNW > 0) {  // the router rows' logits, written in this launch
+      if (threadIdx.x < kWave) {
+        // lane l < kRouterLines watches line l until it holds its count of
+        // router rows (bounded)
+        const int lane = threadIdx.x;
+        const int l = min(lane, kRouterLines - 1);
+        const int need = (f.n_router - l + kRouterLines - 1) / kRouterLines;
+        const long long t0 = clock64();
+        while (!__all(__hip_atomic_load(&f.rdone[l * kCtlStride], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) >= need)) {
+          __builtin_amdgcn_s_sleep(4);
+          if (clock64() - t0 > kWaitCycles) {
+            if (lane == 0) __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+        const __amdgpu_buffer_rsrc_t lr =
+            __builtin_amdgcn_make_buffer_rsrc(f.logits_out, 0, 0x7fffffff, 0x00020000);
+        float lv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = min(lane + kWave * j, f.E - 1);
+          lv[j] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(
+                         lr, static_cast<uint32_t>(b * f.E + e) * 4u, 0, kCpolSc1));
+        }
+        if (f.sel_bias)
+          topk_token_vals<true, decltype(mark), true>(lv, f.sel_bias, f.ids, f.w, nullptr, f.E,
+                                                      f.topk, f.renorm, b, mark);
+        else
+          topk_token_vals<false, decltype(mark), true>(lv, nullptr, f.ids, f.w, nullptr, f.E,
+                                                       f.topk, f.renorm, b, mark);
+      }
     } else if (threadIdx.x < kWave) {
       if (f.sel_bias)
         topk_token<true, decltype(mark), true>(f.logits_in, f.sel_bias, f.ids, f.w, nullptr, f.E,
@@ -128,6 +188,7 @@ __device__ __forceinline__ void route_front(const FfnArgs& a, int b, uint8_t* sm
       }
     }
   }
+  if constexpr (kOne) count_seen(a);
   BucketLds& L = *reinterpret_cast<BucketLds*>(smem);
   int32_t* ids_l = reinterpret_cast<int32_t*>(smem + sizeof(BucketLds));
   bucket_clear(L);
@@ -215,6 +276,120 @@ __device__ __forceinline__ void front_rows(const uint32_t (&mk)[4], int el, int 
   __syncthreads();
 }
 
+// One launch: a down task's y rows are stored through to the coherence point
+// (sc1); once every thread's stores are done, the task counts each of its rows
+// in its token's counter (tokc), d / 64 counts a local pick.
+__device__ __forceinline__ void count_rows(const FfnArgs& a, const uint32_t (&mk)[4], int el,
+                                           int first, int ntok, uint8_t* smem) {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's y stores are done
+  __syncthreads();                     // ... every thread's, and the task's LDS is free
+  int32_t* list = reinterpret_cast<int32_t*>(smem);
+  front_rows(mk, el, first, ntok, list);
+  if (static_cast<int>(threadIdx.x) < ntok)
+    __hip_atomic_fetch_add(&a.tokc[list[threadIdx.x] * kCtlStride], 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kOneMaxVec = 512;  // d <= 4096 in one launch
+struct OneCombineLds {
+  int32_t pp[8];
+  float wt[8];
+  CombineLdsT<kOneMaxVec> c;
+};
+
+// One launch: token t's combine (K3 page, stage "E"), as the launch's last S
+// workgroups. Its pick positions come from the masks, as the bucketing
+// numbers them (expert el's bucket starts at the sum of the counts below el;
+// the token's row in it is the rank of its bit in el's mask), its ids and
+// weights from the top-k workgroups' stores (coherent loads); cnt / mk:
+// wait_route's counts and masks. It waits until its d / 64 rows a local pick
+// are counted (then resets its counter), sums them as moe_combine does, and
+// counts itself; the last combine workgroup waits until every reader of the
+// routing has counted itself and clears the front's control block for the
+// next call.
+__device__ __forceinline__ void combine_one(const FfnArgs& a, int t, int cnt,
+                                            const uint32_t (&mk)[4], int n_readers,
+                                            uint8_t* smem) {
+  OneCombineLds& L = *reinterpret_cast<OneCombineLds*>(smem);
+  const RouteFront& f = a.rf;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x < kWave) {
+    int incl = cnt;
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+      const int o = __shfl_up(incl, m, kWave);
+      if (lane >= m) incl += o;
+    }
+    const int off = incl - cnt;
+    int id = -1;
+    float w = 0.0f;
+    if (lane < f.topk) {
+      const size_t i = static_cast<size_t>(t) * f.topk + lane;
+      id = __hip_atomic_load(&f.ids[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w = __hip_atomic_load(&f.w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int el = id - f.local_base;
+    const bool local = lane < f.topk && el >= 0 && el < a.n_loc;
+    const int src = local ? el : 0;
+    int rank = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t bits = __shfl(mk[i], src, kWave);
+      if (i < (t >> 5)) rank += __popc(bits);
+      else if (i == (t >> 5)) rank += __popc(bits & ((1u << (t & 31)) - 1u));
+    }
+    const int base = __shfl(off, src, kWave);
+    const int n = __popcll(__ballot(local));
+    if (lane < 8) {
+      L.pp[lane] = local ? base + rank : -1;
+      L.wt[lane] = w;
+    }
+    if (lane == 0) {  // this token's y rows
+      int32_t* c = &a.tokc[t * kCtlStride];
+      const int need = (a.d / kRowsPerBlock) * n;
+      const long long t0 = clock64();
+      while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+        __builtin_amdgcn_s_sleep(4);
+        if (clock64() - t0 > kWaitCycles) {
+          __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
+    }
+  }
+  __syncthreads();
+  combine_token_staged<1, true, kSplit * kWave, kOneMaxVec>(a.y, L.wt, L.pp, a.gamma, a.out, a.d,
+                                                            f.topk, a.eps, -1, t, L.c);
+  // the last combine workgroup clears the control block once every reader
+  // of the routing has counted itself
+  __shared__ int last;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(f.cdone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           a.comb - 1;
+  __syncthreads();
+  if (!last) return;
+  if (threadIdx.x < kWave) {
+    const long long t0 = clock64();
+    for (;;) {
+      int v = __hip_atomic_load(&f.seen[lane * kCtlStride], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+      if (v >= n_readers) break;
+      __builtin_amdgcn_s_sleep(4);
+      if (clock64() - t0 > kWaitCycles) {
+        if (lane == 0) __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  int32_t* blk = f.done;  // the front's control block starts with the counter copies
+  for (int i = threadIdx.x; i < kFrontWords; i += blockDim.x)
+    __hip_atomic_store(&blk[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The single launch (no shared expert), items of 16 bucket rows at every S;
 // PG / PD: chunks in flight a wave in gate_up / down tasks. Forward progress:
 // every gate_up workgroup id is below every down workgroup id, and workgroups
@@ -243,35 +418,47 @@ __device__ __forceinline__ void front_rows(const uint32_t (&mk)[4], int el, int 
 #define MOE_SINGLE_PL_LARGE_S 2
 #endif
 // kFront: the routing front runs as the first a.front workgroups, and every
-// other workgroup waits for it.
-template <int PG, int PD, int PL, bool kFront>
+// other workgroup waits for it. kOne (with kFront): the whole block as one
+// launch, the front starting with the router rows (router_row_w4 with RNW
+// float4s a lane a K slice) and the combine as the last a.comb workgroups.
+template <int PG, int PD, int PL, bool kFront, int RNW = 0, bool kOne = false>
 __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_kernel(FfnArgs a) {
   constexpr int TTG = 1;
   constexpr int kRed = static_cast<int>(sizeof(f32x4_t)) * kSplit * TTG * 4 * kWave;
   constexpr int kStage = kSplit * PL * kMxTileBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kRed > kStage ? kRed : kStage];
+  constexpr int kTask = kRed > kStage ? kRed : kStage;
+  constexpr int kComb = kOne ? static_cast<int>(sizeof(OneCombineLds)) : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kTask > kComb ? kTask : kComb];
+  static_assert(!kOne || (kFront && RNW > 0 && PL == 0), "one launch: front, router rows");
   auto red = reinterpret_cast<f32x4_t(*)[TTG][4][kWave]>(smem);
   const int lane = threadIdx.x & (kWave - 1);
   int t = blockIdx.x;
   uint32_t mk[4];
   int cnt;
+  const int RB13 = 2 * a.I / kRowsPerBlock, NC13 = a.d / kChunkK;
+  const int RB2 = a.d / kRowsPerBlock, NC2 = a.I / kChunkK;
   if constexpr (kFront) {
     if (t < a.front) {
-      route_front(a, t, smem);
+      route_front<RNW, kOne>(a, t, smem);
       return;
     }
     t -= a.front;
     cnt = wait_route(a, t, mk);
+    if constexpr (kOne) {
+      const int n_tasks = a.max_work * (RB13 + RB2);
+      if (t >= n_tasks) {  // past every task: the combine
+        if (t - n_tasks < a.comb) combine_one(a, t - n_tasks, cnt, mk, n_tasks + 1, smem);
+        return;
+      }
+      count_seen(a);
+    }
   } else {
     cnt = lane < a.n_loc ? a.counts[lane] : 0;
   }
   const int n_work = count_work<TTG>(cnt);
-  const int RB13 = 2 * a.I / kRowsPerBlock, NC13 = a.d / kChunkK;
-  const int RB2 = a.d / kRowsPerBlock, NC2 = a.I / kChunkK;
-  int el, row0, ntok;
+  int el, row0, ntok, first;
   if (t < n_work * RB13) {
     const int wi = t / RB13, rb = t - wi * RB13;
-    int first;
     find_task<TTG>(cnt, wi, el, row0, ntok, &first);
     const uint8_t* tiles = a.w13 + (static_cast<size_t>(el) * RB13 + rb) * NC13 * kMxTileBytes;
     if constexpr (kFront) {  // the item's tokens from the masks, in LDS (read before red is)
@@ -291,11 +478,13 @@ __global__ __launch_bounds__(kSplit * kWave, MOE_SINGLE_OCC) void ffn_single_ker
   t -= n_work * RB13;
   if (t >= n_work * RB2) return;
   const int wi = t / RB2, rb = t - wi * RB2;
-  find_task<TTG>(cnt, wi, el, row0, ntok);
+  find_task<TTG>(cnt, wi, el, row0, ntok, &first);
   const uint8_t* tiles = a.w2 + (static_cast<size_t>(el) * RB2 + rb) * NC2 * kMxTileBytes;
-  ffn_task<true, TTG, PD, false, true, false, PL>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y, a.d,
-                                       [](int r) { return r; },
-                                       WaitFlag{&a.ready[t * kCtlStride], a.error}, red);
+  ffn_task<true, TTG, PD, false, true, false, PL, kOne>(tiles, NC2, a.h, a.I, row0, ntok, rb, a.y,
+                                                        a.d, [](int r) { return r; },
+                                                        WaitFlag{&a.ready[t * kCtlStride], a.error},
+                                                        red);
+  if constexpr (kOne) count_rows(a, mk, el, first, ntok, smem);
 }
 
 // chunks in flight a wave of the routed tasks in the two launches for
@@ -382,7 +571,7 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a)
   int t = blockIdx.x;
   if constexpr (kFront) {
     if (t < a.front) {
-      route_front(a, t, smem);
+      route_front<0, false>(a, t, smem);
       return;
     }
     t -= a.front;
@@ -547,7 +736,8 @@ FfnLayout ffn_layout(const moe_dims& m) {
   l.hs = round_up(static_cast<size_t>(R) * m.I * 2, 256);
   l.prod = l.hs + round_up(static_cast<size_t>(m.S) * m.shared_I * 2, 256);
   l.ready = l.prod + static_cast<size_t>(l.max_work) * kCtlStride * 4;
-  l.route = l.ready + static_cast<size_t>(l.max_work) * (m.d / kRowsPerBlock) * kCtlStride * 4;
+  l.tokc = l.ready + static_cast<size_t>(l.max_work) * (m.d / kRowsPerBlock) * kCtlStride * 4;
+  l.route = l.tokc + static_cast<size_t>(m.S) * kCtlStride * 4;
   l.error = l.route + round_up(static_cast<size_t>(kFrontWords) * 4, 256);
   l.total = l.error + 256;
   return l;
@@ -589,7 +779,7 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
     f.logits_in = front->logits_in;
     f.parts = front->parts;
     f.KP = front->parts ? router_parts(m) : 0;
-    f.lbias = front->parts ? logit_bias(m, front->bias) : nullptr;
+    f.lbias = front->parts || front->wr ? logit_bias(m, front->bias) : nullptr;
     f.sel_bias = select_bias(m, front->bias);
     f.logits_out = front->logits;
     f.ids = front->ids;
@@ -598,17 +788,34 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
     f.pick_pos = front->pick_pos;
     f.active = front->active;
     f.done = reinterpret_cast<int32_t*>(ws + l.route);
-    f.masks = reinterpret_cast<uint32_t*>(ws + l.route) + kDoneCopies * kCtlStride;
+    int32_t* blk = reinterpret_cast<int32_t*>(ws + l.route);
+    f.masks = reinterpret_cast<uint32_t*>(blk + kFrontMaskWord);
+    f.rdone = blk + kFrontRouterWord;
+    f.seen = blk + kFrontSeenWord;
+    f.cdone = blk + kFrontCombWord;
     f.E = m.E;
     f.topk = m.topk;
     f.renorm = m.renorm;
     f.local_base = m.local_base;
     a.front = m.S + 1;
+    if (front->wr && front->out && one_launch(m)) {  // the whole block as one launch
+      f.wr = front->wr;
+      f.n_router = m.E;
+      a.front += m.E;
+      a.comb = m.S;
+      a.tokc = reinterpret_cast<int32_t*>(ws + l.tokc);
+      a.gamma = front->gamma;
+      a.out = front->out;
+      a.eps = m.eps;
+    }
   }
   if (single_launch(m)) {
     const int tasks = l.max_work * (2 * m.I + m.d) / kRowsPerBlock;
-    const int grid = a.front + tasks;
-    if (a.front) {
+    const int grid = a.front + tasks + a.comb;
+    if (a.comb) {
+      hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, 0, true, 1, true>), dim3(grid),
+                         dim3(kSplit * kWave), 0, stream, a);
+    } else if (a.front) {
       if (m.S > 32)
         hipLaunchKernelGGL((ffn_single_kernel<2, MOE_SINGLE_PD, MOE_SINGLE_PL_LARGE_S, true>),
                            dim3(grid), dim3(kSplit * kWave), 0, stream, a);

@@ -228,8 +228,9 @@ __device__ __forceinline__ void compute_chunk(const BfChunk<TTG>& ch, f32x4_t (&
 
 // Sum of the 4 waves' partial tiles of a task in wave order, then the
 // epilogue: gate_up rounds gate and up to bf16 and writes SwiGLU rows; down
-// writes bf16 rows; kF32Out writes unrounded fp32 rows. Workgroup-level.
-template <int TTG, bool kGateUp, bool kCoh, bool kF32Out>
+// writes bf16 rows (kOutCoh: through to the coherence point, for a combine
+// in the same launch); kF32Out writes unrounded fp32 rows. Workgroup-level.
+template <int TTG, bool kGateUp, bool kCoh, bool kF32Out, bool kOutCoh = false>
 __device__ __forceinline__ void task_epilogue(const f32x4_t (&acc)[TTG][4], int n_tt, int ntok,
                                               int row0, int rb, uint16_t* __restrict__ out,
                                               int out_ld, f32x4_t (*red)[TTG][4][kWave]) {
@@ -272,8 +273,12 @@ __device__ __forceinline__ void task_epilogue(const f32x4_t (&acc)[TTG][4], int 
         __hip_atomic_store(frow + i, s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       const int n0 = kRowsPerBlock * rb + 16 * r + 4 * g;
-      *reinterpret_cast<u32x2_t*>(orow + n0) =
-          u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+      const u32x2_t v{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+      if constexpr (kOutCoh)
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(orow + n0), __builtin_bit_cast(uint64_t, v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        *reinterpret_cast<u32x2_t*>(orow + n0) = v;
     }
   }
 }
@@ -296,8 +301,9 @@ struct NoWait {
 // are read from there when the ring takes them: a task that waits (a down task
 // of the single launch) then has P + PL chunks in flight at the register cost
 // of P. The LDS is read only after every vector load of the wave has arrived.
+// kOutCoh (down): the output rows go through to the coherence point.
 template <bool kMx, int TTG, int P, bool kGateUp, bool kCoh, bool kF32Out = false, int PL = 0,
-          class SrcOf, class BeforeB>
+          bool kOutCoh = false, class SrcOf, class BeforeB>
 __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int NC,
                                          const uint16_t* __restrict__ bsrc, int K, int row0,
                                          int ntok, int rb, uint16_t* __restrict__ out, int out_ld,
@@ -380,7 +386,7 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
   for (int i = 0; i < P; ++i)
     if (j0 + P + i < my_n) compute_chunk<TTG>(ring[i], acc, n_tt);
 
-  task_epilogue<TTG, kGateUp, kCoh, kF32Out>(acc, n_tt, ntok, row0, rb, out, out_ld, red);
+  task_epilogue<TTG, kGateUp, kCoh, kF32Out, kOutCoh>(acc, n_tt, ntok, row0, rb, out, out_ld, red);
 }
 
 // ---------------------------------------------------------------------------

@@ -23,18 +23,43 @@ constexpr int kSharedP = MOE_SHARED_P;
 // rank-th set bit of its expert's mask, as the bucketing numbers them), so
 // the bucketing, which writes the ABI's bucket outputs, is not on their path.
 // The counter (kDoneCopies copies, one 128-byte line each) and the masks are
-// cleared by the router launch before this one.
+// zero when the launch starts: a call leaves them at zero for the next one
+// (moe_forward's combine launch clears them).
+//
+// The whole block as one launch (moe_forward_one_launch: no shared expert,
+// S <= 16, d <= 4096; K3 page, module docstring: the layer as one persistent
+// launch): the router itself runs at the head of the front, as E workgroups
+// of one router row each (summed exactly as the router launch sums it), and
+// the combine as the launch's last S workgroups (one a token). The top-k
+// workgroups wait for the router rows' count, kept on kRouterLines lines
+// (router row b counts on line b mod kRouterLines: device-scope atomics on
+// one address serialise, about 3.4 us for 256 of them, measured). Every
+// workgroup that reads the routing counts itself on the kSeenLines lines once
+// it has; the last combine workgroup waits for that count and clears the
+// control block for the next call.
 constexpr int kDoneCopies = 8;
 constexpr int kMaskWordsAll = 32 * 4;  // 32 local experts x 128 tokens
-// words of the front's control block: the counter copies, then the masks
-constexpr int kFrontWords = kDoneCopies * 32 + kMaskWordsAll;
+constexpr int kRouterLines = 32;
+constexpr int kSeenLines = 64;
+// words of the front's control block: the counter copies, the masks, then
+// (one launch) the router rows' lines, the seen lines and the combine count
+constexpr int kFrontMaskWord = kDoneCopies * 32;
+constexpr int kFrontRouterWord = kFrontMaskWord + kMaskWordsAll;
+constexpr int kFrontSeenWord = kFrontRouterWord + kRouterLines * 32;
+constexpr int kFrontCombWord = kFrontSeenWord + kSeenLines * 32;
+constexpr int kFrontWords = kFrontCombWord + 32;
 struct RouteFront {
   const float* logits_in;  // no K parts: the router's logits
   const float* parts;      // else the router's K parts [KP][S][E]
   int KP;
-  const float* lbias;      // K parts: the logit bias (added by the top-k), or NULL
+  const float* lbias;      // K parts or router rows: the logit bias, or NULL
   const float* sel_bias;   // selection-only bias, or NULL
-  float* logits_out;       // K parts: the summed logits
+  float* logits_out;       // K parts: the summed logits; router rows: the logits
+  const float* wr;         // router rows: the router weights [E][d]
+  int n_router;            // workgroups of router rows (E), or 0
+  int32_t* rdone;          // workspace: the router rows' lines
+  int32_t* seen;           // workspace: the seen lines (one launch)
+  int32_t* cdone;          // workspace: combine workgroups done (one launch)
   int32_t* ids;
   float* w;
   int32_t* offsets;
@@ -60,8 +85,14 @@ struct FfnArgs {
   int32_t* ready;  // workspace: a flag a down task: its item's SwiGLU rows are written
   int32_t* error;  // workspace: nonzero if a wait hit its bound
   int S, d, I, Is, n_loc, R_max, max_work;
-  int front;       // workgroups of the routing front (S + 1), 0 without one
+  int front;       // workgroups of the routing front (router rows + S + 1), 0 without one
   RouteFront rf;
+  // one launch: the combine as the last comb workgroups (S, or 0 without)
+  int comb;
+  int32_t* tokc;          // workspace: y rows written, a token (one line each)
+  const uint16_t* gamma;  // post-expert norm weight [d] bf16, or NULL
+  float* out;             // [S][d] fp32
+  float eps;
 };
 
 // ints between two counters or flags (one 128-byte line each)
@@ -69,11 +100,12 @@ constexpr int kCtlStride = 32;
 
 // workspace: SwiGLU rows h [R_max][I] and hs [S][Is] (bf16), then the
 // counters prod (max_work lines), the ready flags (max_work * d / 64 lines),
-// the routing front's control block (kFrontWords words) and the error word;
-// these must start at zero and are left at zero (the front's block is
-// cleared by moe_forward's router launch)
+// the token counters of the combine (S lines), the routing front's control
+// block (kFrontWords words) and the error word; these must start at zero and
+// are left at zero (the front's block is cleared by moe_forward's combine
+// launch, or in one launch by its last combine workgroup)
 struct FfnLayout {
-  size_t h, hs, prod, ready, route, error, total;
+  size_t h, hs, prod, ready, tokc, route, error, total;
   int max_work;
 };
 
@@ -99,6 +131,9 @@ FfnLayout ffn_layout(const moe_dims& m);
 struct FrontIo {
   const float* logits_in;
   const float* parts;
+  const float* wr;        // one launch: the router weights (the router rows), else NULL
+  float* out;             // one launch: the combine's output [S][d], else NULL
+  const uint16_t* gamma;  // one launch: the post-expert norm weight, or NULL
   const float* bias;  // the caller's bias (split by bias_mode)
   float* logits;
   int32_t* ids;
@@ -108,8 +143,12 @@ struct FrontIo {
   int32_t* active;
 };
 
+// moe_forward_one_launch: the whole block as one launch (FrontIo.wr and
+// .out), without a shared expert at S <= 16 and d <= 4096
+inline bool one_launch(const moe_dims& m) { return m.shared_I == 0 && m.S <= 16 && m.d <= 4096; }
+
 // the control block of the FFN launch's front (kFrontWords words), which the
-// router launch before it clears
+// combine launch after it clears
 int32_t* route_front_block(const moe_dims& m, void* workspace);
 
 // enqueue the expert FFNs (after argument checks); error_word: where a wait

@@ -10,7 +10,12 @@
 //      wait for them on flags in the workspace, the shared expert's tasks do
 //      not (K3 page, stage "route": the routing runs inside the persistent
 //      launch that consumes it)
-//   3  per-pick RMSNorm and the weighted sum (one workgroup a token)
+//   3  per-pick RMSNorm and the weighted sum (one workgroup a token), whose
+//      workgroup 0 leaves the front's control block at zero for the next call
+//
+// moe_forward_one_launch runs all of it as one launch (S <= 16, d <= 4096, no
+// shared expert): the router rows at the head of the front, the combine as
+// the launch's last workgroups.
 //
 // The outputs are those of moe_route, moe_bucket, moe_expert_ffn and
 // moe_combine, bit for bit: the same device code computes every value.
@@ -77,20 +82,32 @@ int forward_enqueue(const moe_dims& m, const void* x, const float* w_router, con
                     const void* ws2_packed, const void* gamma, float* logits, int32_t* topk_ids,
                     float* topk_w, int32_t* counts, int32_t* offsets, int32_t* rows,
                     int32_t* pick_pos, int32_t* active, void* y, float* out, void* workspace,
-                    hipStream_t stream, int32_t* error_word) {
+                    hipStream_t stream, int32_t* error_word, bool one = false) {
   const size_t parts_bytes = router_parts_bytes(m);
   float* parts = parts_bytes ? static_cast<float*>(workspace) : nullptr;
   void* ffn_ws = static_cast<uint8_t*>(workspace) + parts_bytes;
   int frc;
-  if (routing_front(m)) {
-    // the router launch also clears the control block of the FFN launch's front
-    launch_router_logits(m, x, w_router, bias, logits, stream, parts,
-                         route_front_block(m, ffn_ws), kFrontWords, 1);
-    // the top-k and the bucketing run at the head of the expert-FFN launch
-    const FrontIo fio{parts ? nullptr : logits, parts, bias, logits, topk_ids, topk_w, offsets,
-                      pick_pos, active};
+  if (one) {
+    // the whole block in the expert-FFN launch: router rows, top-k and
+    // bucketing at its head, the combine at its tail; its last combine
+    // workgroup leaves the front's control block at zero for the next call
+    const FrontIo fio{nullptr, nullptr, w_router, out, static_cast<const uint16_t*>(gamma), bias,
+                      logits, topk_ids, topk_w, offsets, pick_pos, active};
     frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y, ffn_ws,
                      stream, error_word, &fio);
+    return frc ? frc : launch_status();
+  }
+  int32_t* front_block = nullptr;
+  if (routing_front(m)) {
+    launch_router_logits(m, x, w_router, bias, logits, stream, parts);
+    // the top-k and the bucketing run at the head of the expert-FFN launch;
+    // its control block is zero at the start of the call and the combine
+    // launch leaves it at zero again
+    const FrontIo fio{parts ? nullptr : logits, parts, nullptr, nullptr, nullptr, bias, logits,
+                      topk_ids, topk_w, offsets, pick_pos, active};
+    frc = launch_ffn(m, x, w13_packed, w2_packed, ws13_packed, ws2_packed, counts, rows, y, ffn_ws,
+                     stream, error_word, &fio);
+    front_block = route_front_block(m, ffn_ws);
   } else {  // the four calls' launches
     launch_router_logits(m, x, w_router, bias, logits, stream, parts);
     launch_topk(m, logits, bias, topk_ids, topk_w, stream, parts, logits);
@@ -99,7 +116,8 @@ int forward_enqueue(const moe_dims& m, const void* x, const float* w_router, con
                      stream, error_word);
   }
   if (frc) return frc;
-  launch_combine(m, y, topk_w, pick_pos, gamma, out, stream);
+  launch_combine(m, y, topk_w, pick_pos, gamma, out, stream, front_block,
+                 front_block ? kFrontWords : 0);
   return launch_status();
 }
 
@@ -155,6 +173,28 @@ extern "C" int moe_forward(const moe_dims* dims, const void* x, const float* w_r
   return forward_enqueue(*dims, x, w_router, bias, w13_packed, w2_packed, ws13_packed, ws2_packed,
                          gamma, logits, topk_ids, topk_w, counts, offsets, rows, pick_pos, active,
                          y, out, workspace, stream, nullptr);
+}
+
+extern "C" int moe_forward_one_launch(const moe_dims* dims, const void* x, const float* w_router,
+                                      const float* bias, const void* w13_packed,
+                                      const void* w2_packed, const void* gamma, float* logits,
+                                      int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                      int32_t* offsets, int32_t* rows, int32_t* pick_pos,
+                                      int32_t* active, void* y, float* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  const int dc = check_dims(dims);
+  if (dc) return dc;
+  MOE_REQUIRE(one_launch(*dims), MOE_ERR_UNSUPPORTED);
+  const int rc = check_forward_args(dims, x, w_router, bias, w13_packed, w2_packed, nullptr, nullptr,
+                                    gamma, logits, topk_ids, topk_w, counts, offsets, rows,
+                                    pick_pos, active, y, out);
+  if (rc) return rc;
+  MOE_REQUIRE(workspace, MOE_ERR_NULL);
+  MOE_REQUIRE(aligned16(workspace), MOE_ERR_ALIGN);
+  MOE_REQUIRE(workspace_bytes >= moe_forward_workspace_bytes(dims), MOE_ERR_WORKSPACE);
+  return forward_enqueue(*dims, x, w_router, bias, w13_packed, w2_packed, nullptr, nullptr, gamma,
+                         logits, topk_ids, topk_w, counts, offsets, rows, pick_pos, active, y, out,
+                         workspace, stream, nullptr, true);
 }
 
 extern "C" int moe_forward_static(const moe_dims* dims, const void* x, const float* w_router,

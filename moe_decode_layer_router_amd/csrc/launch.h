@@ -56,18 +56,18 @@ inline size_t router_parts_bytes(const moe_dims& m) {
 // `parts` (router_parts_bytes of scratch) and S > kRouteSplitMinS the router
 // writes its K parts there and the top-k sums them into `logits_out`;
 // otherwise the router writes `logits` itself.
-// clear: n_clear words clear_stride apart that workgroup 0 sets to zero (the
-// routing-ready flags of moe_forward's FFN launch), or NULL
 void launch_router_logits(const moe_dims& m, const void* x, const float* wr, const float* bias,
-                          float* logits, hipStream_t stream, float* parts = nullptr,
-                          int32_t* clear = nullptr, int n_clear = 0, int clear_stride = 1);
+                          float* logits, hipStream_t stream, float* parts = nullptr);
 void launch_topk(const moe_dims& m, const float* logits, const float* bias, int32_t* ids, float* w,
                  hipStream_t stream, const float* parts = nullptr, float* logits_out = nullptr);
 void launch_bucket(const moe_dims& m, const int32_t* ids, int32_t* counts, int32_t* offsets,
                    int32_t* rows, int32_t* pick_pos, int32_t* active, hipStream_t stream);
 // dense bf16 [N][K] -> the bf16 tile order (the down-projection row order)
 void launch_pack_bf16(const uint16_t* w, void* packed, int N, int K, hipStream_t stream);
+// clear: n_clear words that workgroup 0 sets to zero (the control block of
+// moe_forward's routing front, for its next call), or NULL
 void launch_combine(const moe_dims& m, const void* y, const float* w, const int32_t* pick_pos,
-                    const void* gamma, float* out, hipStream_t stream);
+                    const void* gamma, float* out, hipStream_t stream, int32_t* clear = nullptr,
+                    int n_clear = 0);
 
 }  // namespace moeblk

@@ -6,26 +6,12 @@
 namespace moeblk {
 namespace {
 
-// Words of the next launch (moe_forward's FFN launch: its routing-ready
-// flags) that must start at zero, cleared by workgroup 0 of the router launch
-// (plain stores: the launch boundary publishes them). n words, stride words
-// apart.
-struct ClearWords {
-  int32_t* p;
-  int n, stride;
-  __device__ void operator()() const {
-    if (p && blockIdx.x == 0 && blockIdx.y == 0)
-      for (int i = threadIdx.x; i < n; i += blockDim.x) p[i * stride] = 0;
-  }
-};
-
 // one workgroup an expert row: the row streams from HBM once, all of it in
 // flight at once; every workgroup reads all of x (through L2)
 template <int NW>
 __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
-    float* __restrict__ logits, int S, int d, int E, ClearWords clr) {
-  clr();
+    float* __restrict__ logits, int S, int d, int E) {
   __shared__ float red[kMaxRouteTiles][kRouteWaves][kTok];
   // NW = 4 (d > 8192): one tile buffer, for the register budget
   router_row<NW, (NW <= 2)>(x, wr, bias, logits, S, d, E, blockIdx.x, red);
@@ -35,8 +21,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 template <int NW, int NE>
 __global__ __launch_bounds__(kRouteThreads) void router_block_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
-    float* __restrict__ logits, int S, int d, int E, ClearWords clr) {
-  clr();
+    float* __restrict__ logits, int S, int d, int E) {
   __shared__ float red[(kRouteBlockTok / kTok) * NE][kRouteWaves][kTok];
   router_block<NW, NE>(x, wr, bias, logits, S, d, E, NE * blockIdx.x, kRouteBlockTok * blockIdx.y,
                        red);
@@ -44,23 +29,23 @@ __global__ __launch_bounds__(kRouteThreads) void router_block_kernel(
 
 template <int NW, int NE>
 void launch_block(const moe_dims& m, const uint16_t* x, const float* wr, const float* bias,
-                  float* logits, hipStream_t stream, ClearWords clr) {
+                  float* logits, hipStream_t stream) {
   hipLaunchKernelGGL((router_block_kernel<NW, NE>), dim3((m.E + NE - 1) / NE,
                      (m.S + kRouteBlockTok - 1) / kRouteBlockTok), dim3(kRouteThreads), 0, stream,
-                     x, wr, bias, logits, m.S, m.d, m.E, clr);
+                     x, wr, bias, logits, m.S, m.d, m.E);
 }
 
 // NE: router rows a workgroup, so that about E * S / 16 / NE ~ E workgroups
 // (at most 2 rows for d > 8192, for the register budget)
 template <int NW>
 void launch_blocks(const moe_dims& m, const uint16_t* x, const float* wr, const float* bias,
-                   float* logits, hipStream_t stream, ClearWords clr) {
+                   float* logits, hipStream_t stream) {
   if constexpr (NW >= 4) {
-    launch_block<NW, 2>(m, x, wr, bias, logits, stream, clr);
+    launch_block<NW, 2>(m, x, wr, bias, logits, stream);
   } else {
-    if (m.S <= 32) launch_block<NW, 2>(m, x, wr, bias, logits, stream, clr);
-    else if (m.S <= 64) launch_block<NW, 4>(m, x, wr, bias, logits, stream, clr);
-    else launch_block<NW, 8>(m, x, wr, bias, logits, stream, clr);
+    if (m.S <= 32) launch_block<NW, 2>(m, x, wr, bias, logits, stream);
+    else if (m.S <= 64) launch_block<NW, 4>(m, x, wr, bias, logits, stream);
+    else launch_block<NW, 8>(m, x, wr, bias, logits, stream);
   }
 }
 
@@ -69,8 +54,7 @@ void launch_blocks(const moe_dims& m, const uint16_t* x, const float* wr, const 
 template <int TT>
 __global__ __launch_bounds__(4 * kWave) void router_split_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, float* __restrict__ parts, int S,
-    int d, int E, int Kp, int n_tt, int n_et, ClearWords clr) {
-  clr();
+    int d, int E, int Kp, int n_tt, int n_et) {
   int b = blockIdx.x;
   const int tt = b % n_tt;
   b /= n_tt;
@@ -80,11 +64,11 @@ __global__ __launch_bounds__(4 * kWave) void router_split_kernel(
 
 template <int TT>
 void launch_split(const moe_dims& m, const uint16_t* x, const float* wr, float* parts,
-                  hipStream_t stream, ClearWords clr) {
+                  hipStream_t stream) {
   const int P = router_parts(m);
   const int n_tt = (m.S + TT - 1) / TT, n_et = (m.E + kRouteTileE - 1) / kRouteTileE;
   hipLaunchKernelGGL((router_split_kernel<TT>), dim3(n_tt * n_et * P), dim3(4 * kWave), 0, stream,
-                     x, wr, parts, m.S, m.d, m.E, m.d / P, n_tt, n_et, clr);
+                     x, wr, parts, m.S, m.d, m.E, m.d / P, n_tt, n_et);
 }
 
 // one token a workgroup: the sum of its router parts (+ the logit bias) into
@@ -117,36 +101,34 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 template <int NW>
 void launch_router(const moe_dims& m, const uint16_t* x, const float* wr, const float* bias,
-                   float* logits, hipStream_t stream, ClearWords clr) {
+                   float* logits, hipStream_t stream) {
   hipLaunchKernelGGL(router_logits_kernel<NW>, dim3(m.E), dim3(kRouteThreads), 0, stream, x, wr,
-                     bias, logits, m.S, m.d, m.E, clr);
+                     bias, logits, m.S, m.d, m.E);
 }
 
 }  // namespace
 
 void launch_router_logits(const moe_dims& m, const void* x, const float* wr, const float* bias,
-                          float* logits, hipStream_t stream, float* parts, int32_t* clear,
-                          int n_clear, int clear_stride) {
-  const ClearWords clr{clear, n_clear, clear_stride};
+                          float* logits, hipStream_t stream, float* parts) {
   bias = logit_bias(m, bias);
   const uint16_t* xx = static_cast<const uint16_t*>(x);
   if (parts && router_parts(m) > 0) {  // the top-k adds the bias
-    if (router_tile_tok(m.S) == 32) launch_split<32>(m, xx, wr, parts, stream, clr);
-    else launch_split<64>(m, xx, wr, parts, stream, clr);
+    if (router_tile_tok(m.S) == 32) launch_split<32>(m, xx, wr, parts, stream);
+    else launch_split<64>(m, xx, wr, parts, stream);
     return;
   }
   if (m.S > kRouteBlockTok) {
     switch (router_nw(m.d)) {
-      case 1: launch_blocks<1>(m, xx, wr, bias, logits, stream, clr); break;
-      case 2: launch_blocks<2>(m, xx, wr, bias, logits, stream, clr); break;
-      default: launch_blocks<4>(m, xx, wr, bias, logits, stream, clr); break;
+      case 1: launch_blocks<1>(m, xx, wr, bias, logits, stream); break;
+      case 2: launch_blocks<2>(m, xx, wr, bias, logits, stream); break;
+      default: launch_blocks<4>(m, xx, wr, bias, logits, stream); break;
     }
     return;
   }
   switch (router_nw(m.d)) {
-    case 1: launch_router<1>(m, xx, wr, bias, logits, stream, clr); break;
-    case 2: launch_router<2>(m, xx, wr, bias, logits, stream, clr); break;
-    default: launch_router<4>(m, xx, wr, bias, logits, stream, clr); break;
+    case 1: launch_router<1>(m, xx, wr, bias, logits, stream); break;
+    case 2: launch_router<2>(m, xx, wr, bias, logits, stream); break;
+    default: launch_router<4>(m, xx, wr, bias, logits, stream); break;
   }
 }
 

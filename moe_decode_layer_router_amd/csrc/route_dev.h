@@ -231,6 +231,75 @@ __device__ __forceinline__ void router_block(const uint16_t* __restrict__ x,
   }
 }
 
+// router_row's logits of expert row e for all S tokens, bit for bit, from a
+// workgroup of 4 waves (moe_forward's expert-FFN launch): wave w sums the K
+// slices 4w .. 4w + 3 of the 16, each exactly as router_row's wave of that
+// index sums it, with the activation tiles of SIF slices in flight at once;
+// the same pairwise tree then adds the 16 slice sums. The logits are stored
+// through to the coherence point, for other workgroups of the launch.
+template <int NW, int SIF>
+__device__ __forceinline__ void router_row_w4(const uint16_t* __restrict__ x,
+                                              const float* __restrict__ wr,
+                                              const float* __restrict__ bias,
+                                              float* __restrict__ logits, int S, int d, int E,
+                                              int e, float (*red)[kRouteWaves][kTok]) {
+  constexpr int kVs = kRouteWaves / 4;  // slices a wave
+  static_assert(kVs % SIF == 0, "slices in flight divide a wave's slices");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int kq = d / kRouteWaves;
+  const int nf = kq / 4;
+  int f[NW];
+  bool live[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    live[i] = lane + kWave * i < nf;
+    f[i] = min(lane + kWave * i, nf - 1);
+  }
+  const float* wrow = wr + static_cast<size_t>(e) * d + kVs * w * kq;
+  f32x4_t wv[kVs][NW];
+#pragma unroll
+  for (int s = 0; s < kVs; ++s)
+#pragma unroll
+    for (int i = 0; i < NW; ++i) wv[s][i] = ld_nt<f32x4_t>(wrow + s * kq + 4 * f[i]);
+  const float b = bias ? bias[e] : 0.0f;
+  const int tok = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+  const int n_tiles = (S + kTok - 1) / kTok;
+  for (int tile = 0; tile < n_tiles; ++tile) {
+#pragma unroll
+    for (int s0 = 0; s0 < kVs; s0 += SIF) {
+      uint2 xv[SIF][kTok][NW];
+#pragma unroll
+      for (int sl = 0; sl < SIF; ++sl)
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+          const uint16_t* xr = x + static_cast<size_t>(min(tile * kTok + t, S - 1)) * d +
+                               (kVs * w + s0 + sl) * kq;
+#pragma unroll
+          for (int i = 0; i < NW; ++i) xv[sl][t][i] = *reinterpret_cast<const uint2*>(xr + 4 * f[i]);
+        }
+#pragma unroll
+      for (int sl = 0; sl < SIF; ++sl) {
+        float acc[kTok];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+          acc[t] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NW; ++i)
+            if (live[i]) acc[t] = dot4(xv[sl][t][i], wv[s0 + sl][i], acc[t]);
+        }
+        const float v = reduce8(acc, lane);
+        if ((lane & 7) == 0) red[tile][kVs * w + s0 + sl][tok] = v;
+      }
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < S; t += blockDim.x)
+    __hip_atomic_store(&logits[static_cast<size_t>(t) * E + e],
+                       slice_tree<kRouteWaves>(red[t / kTok], t % kTok) + b, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // A logit as an unsigned key with the same order; -0 is folded into +0 so
 // that both compare equal. Finite logits never map to 0.
 __device__ __forceinline__ uint32_t order_key(float l) {
@@ -304,8 +373,8 @@ __device__ __forceinline__ void order2(uint32_t& ka, int& ia, float& la, uint32_
 // mark(id, t) runs for each of the token's ids (lanes < topk).
 // topk_token_vals: the same with the token's logits already in registers
 // (lane l: lv[j] = logit of expert l + 64 j, any value for ids >= E).
-// kCohIds: the ids are stored through to the coherence point (sc1), for
-// another workgroup of the same launch to read.
+// kCohIds: the ids and weights are stored through to the coherence point
+// (sc1), for other workgroups of the same launch to read.
 template <bool kSel, class Mark, bool kCohIds = false>
 __device__ __forceinline__ void topk_token_vals(const float (&lv)[4],
                                                 const float* __restrict__ sel_bias,
@@ -394,7 +463,12 @@ __device__ __forceinline__ void topk_token_vals(const float (&lv)[4],
       ids[static_cast<size_t>(t) * topk + lane] = my_id;
     if (ids_lds) ids_lds[t * topk + lane] = my_id;
     mark(my_id, t);
-    w[static_cast<size_t>(t) * topk + lane] = renorm ? sc / sum : sc;
+    const float wv = renorm ? sc / sum : sc;
+    if constexpr (kCohIds)
+      __hip_atomic_store(&w[static_cast<size_t>(t) * topk + lane], wv, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else
+      w[static_cast<size_t>(t) * topk + lane] = wv;
   }
 }
 

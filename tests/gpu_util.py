@@ -42,11 +42,14 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def run_gpu(inp: dict, blk: MoeBlock | None = None, fused: bool = False) -> dict:
+def run_gpu(inp: dict, blk: MoeBlock | None = None, fused: bool | str = False) -> dict:
     """One step of the block on the GPU: the four calls, or (fused) through
-    moe_forward. The SwiGLU rows are read from the call's workspace."""
+    moe_forward, or (fused="one") through moe_forward_one_launch. The SwiGLU
+    rows are read from the call's workspace."""
     blk = blk or MoeBlock(inp)
-    if fused:
+    if fused == "one":
+        blk.forward_one_launch()
+    elif fused:
         blk.forward()
     else:
         blk.step()

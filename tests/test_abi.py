@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert mb.moe_abi_version() == mb.ABI_VERSION == 3
+    assert mb.moe_abi_version() == mb.ABI_VERSION == 4
     for code in range(-6, 1):
         s = mb.moe_status_string(code)
         assert s and s != "unknown status"
@@ -319,6 +319,33 @@ def test_forward_rejects():
     assert call(d, ok, need - 1) == mb.MOE_ERR_WORKSPACE
     d4 = mb.dims_from(CONFIGS["s128_shared"])  # a shared expert needs its weights
     assert call(d4, ok, mb.moe_forward_workspace_bytes(d4)) == mb.MOE_ERR_NULL
+
+
+def test_one_launch_rejects():
+    """moe_forward_one_launch: moe_forward's checks, and MOE_ERR_UNSUPPORTED
+    outside S <= 16, d <= 4096 without a shared expert (before anything is
+    enqueued)."""
+    d = dims(S=16, d=4096, shared_I=0)
+    need = mb.moe_forward_workspace_bytes(d)
+    # x, w_router, bias, w13, w2, gamma, logits, ids, w, counts, offsets,
+    # rows, pick_pos, active, y, out, workspace
+    ok = [FAKE, FAKE, None, FAKE, FAKE, None] + [FAKE] * 11
+    call = lambda dd, a, n=need: _rc("moe_forward_one_launch", ctypes.byref(dd), *a, n, None)  # noqa: E731
+    assert call(dims(S=0), ok) == mb.MOE_ERR_SHAPE
+    for bad in (dims(S=17, d=4096, shared_I=0), dims(S=16, d=4224, shared_I=0),
+                dims(S=8, d=1024, shared_I=256)):
+        assert call(bad, ok, mb.moe_forward_workspace_bytes(bad)) == mb.MOE_ERR_UNSUPPORTED
+    for i in [0, 1, 3, 4] + list(range(6, 17)):
+        a = list(ok)
+        a[i] = None
+        assert call(d, a) == mb.MOE_ERR_NULL, i
+        a[i] = MIS
+        assert call(d, a) == mb.MOE_ERR_ALIGN, i
+    for i in (2, 5):  # optional pointers: misaligned is still an error
+        a = list(ok)
+        a[i] = MIS
+        assert call(d, a) == mb.MOE_ERR_ALIGN, i
+    assert call(d, ok, need - 1) == mb.MOE_ERR_WORKSPACE
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path):

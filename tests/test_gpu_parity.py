@@ -302,6 +302,55 @@ def test_fused_repeated_calls_agree():
         assert np.array_equal(outs[0], o)
 
 
+# ------------------------------------------------- moe_forward_one_launch
+
+# S <= 16, d <= 4096, no shared expert: ragged S, one token, tokens without a
+# local pick, a token with all 8 picks local (two staged batches in the
+# combine), few router rows (E = 8), d = 640 and 4096, the selection-only bias
+ONE = {k: FUSED[k] for k in ("tiny", "S13_ragged", "d640_I256", "no_local", "S1", "some_local",
+                             "d4096_S16", "sel_bias_S16")}
+ONE["eight_local_picks"] = EDGE["eight_local_picks"]
+ONE["E8_S16"] = _tiny(S=16, E=8, n_local=8, topk=4)
+
+
+@pytest.mark.parametrize("name", list(ONE))
+def test_one_launch_equals_forward(name):
+    """The block as one launch gives moe_forward's outputs bit for bit (the
+    same device code computes every value), twice in a row on one workspace
+    (its last combine workgroup leaves the control words at zero), and
+    matches the oracle."""
+    inp = make_inputs(ONE[name], 17, gamma="random")
+    gf = run_gpu(inp, fused=True)
+    blk = gf["blk"]
+    for rep in range(2):
+        blk.out.fill_(float("nan"))
+        g1 = run_gpu(inp, blk, fused="one")
+        for k in KEYS:
+            assert np.array_equal(g1[k], gf[k]), (rep, k)
+        n = int(gf["offsets"][-1])
+        assert np.array_equal(g1["y"][:n], gf["y"][:n]), rep
+    check_block(inp, g1)
+
+
+@pytest.mark.parametrize("name", ["s8_uniform", "s16_local25"])
+def test_one_launch_full_workload(name):
+    """The S = 8 and S = 16 workloads at full size, one launch against
+    moe_forward (itself checked against the oracle at full size), every
+    output compared, three calls in a row with moe_forward in between."""
+    inp = make_inputs(get_config(name), 0, gamma="random")
+    gf = run_gpu(inp, fused=True)
+    blk = gf["blk"]
+    for rep in range(3):
+        g1 = run_gpu(inp, blk, fused="one")
+        for k in KEYS:
+            assert np.array_equal(g1[k], gf[k]), (rep, k)
+        n = int(gf["offsets"][-1])
+        assert np.array_equal(g1["y"][:n], gf["y"][:n]), rep
+        if rep == 1:  # moe_forward on the workspace the one launch left behind
+            g2 = run_gpu(inp, blk, fused=True)
+            assert np.array_equal(g2["out"], gf["out"])
+
+
 # Bucket sizes on both sides of the limits of the routed tasks that stage their
 # rows in LDS, in the launches with a shared expert (at most 16 rows, and
 # rows x K x 2 bytes at most 64 KiB; at S > 16 48 KiB in gate_up and 32 KiB in
