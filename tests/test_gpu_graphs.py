@@ -1,8 +1,8 @@
 """HIP graph capture of the library's calls.
 
-moe_forward and the steps around the block make no memset or allocation and
-leave their counters and flags at zero inside every launch, so they can be
-captured. Each test captures the calls once, replays the graph several times
+moe_forward, moe_forward_one_launch and the steps around the block make no
+memset or allocation and leave their counters and flags at zero by the end
+of every call (with kernel stores), so they can be captured. Each test captures the calls once, replays the graph several times
 with eager calls of the same entry points between the replays, poisons the
 outputs before every replay, and checks every replay against the eager
 result bit for bit."""
@@ -58,6 +58,34 @@ def test_forward_graph_replays_match_eager(name):
         torch.cuda.synchronize()
         assert np.array_equal(to_np(blk.out), ref["out"]), (name, i, "eager")
     assert blk.forward_error() == 0 and blk.ffn_error() == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "s8_uniform"])
+def test_one_launch_graph_replays_match_eager(name):
+    """The block as one launch: its last combine workgroup clears the control
+    words for the next call, also between graph replays; moe_forward runs
+    eagerly on the same workspace in between."""
+    from moe_decode_layer_router_amd.block import MoeBlock
+
+    inp = make_inputs(get_config(name), 0, gamma="random")
+    blk = MoeBlock(inp)
+    blk.forward_one_launch()
+    torch.cuda.synchronize()
+    ref = _snapshot(blk, KEYS)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        blk.forward_one_launch()
+    for i in range(3):
+        _poison(blk, KEYS)
+        g.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(blk, KEYS)
+        for k in KEYS:
+            assert np.array_equal(got[k], ref[k]), (name, i, k)
+        blk.forward() if i % 2 else blk.forward_one_launch()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(blk.out), ref["out"]), (name, i, "eager")
+    assert blk.forward_error() == 0
 
 
 def test_steps_around_block_graph_replays_match_eager():
