@@ -251,8 +251,11 @@ size_t moe_forward_workspace_bytes(const moe_dims* dims);
  * calls, with identical values (the same device code computes every value).
  * `workspace` follows the moe_expert_ffn rules (zero-filled once before first
  * use, error word at byte moe_forward_workspace_bytes - 256, calls sharing it
- * must not overlap); a workspace used with other dims must be zero-filled
- * again. */
+ * must not overlap): the expert-FFN launch's counters and flags return to
+ * zero within it, and the combine launch clears the routing front's control
+ * words for the next call (so moe_forward and moe_forward_one_launch may take
+ * turns on one workspace); a workspace used with other dims must be
+ * zero-filled again. */
 int moe_forward(const moe_dims* dims, const void* x, const float* w_router, const float* bias,
                 const void* w13_packed, const void* w2_packed, const void* ws13_packed,
                 const void* ws2_packed, const void* gamma, float* logits, int32_t* topk_ids,
