@@ -517,13 +517,15 @@ constexpr int kPairLdsB = 65536;
 #define MOE_PAIR_TT1_P 2
 #endif
 
-// LDS of the two launches: the partial tiles of the reduction, or the B rows
-// of a routed task that stages them
-template <int TTG, int kLdsB = kPairLdsB>
+// LDS of the two launches: the partial tiles of the reduction, the B rows of
+// a routed task that stages them, or the shared task's staged rows of SG
+// tokens (0: none)
+template <int TTG, int kLdsB = kPairLdsB, int SG = 0>
 constexpr int pair_smem() {
   constexpr int red = static_cast<int>(sizeof(f32x4_t)) * kSplit *
                       (kSharedTTG > TTG ? kSharedTTG : TTG) * 4 * kWave;
-  return red > ldsb_smem<kLdsB>() ? red : ldsb_smem<kLdsB>();
+  constexpr int m = red > ldsb_smem<kLdsB>() ? red : ldsb_smem<kLdsB>();
+  return SG > 0 && sd_smem<SG>() > m ? sd_smem<SG>() : m;
 }
 
 // With 32-row items (S > 16) the down launch runs the shared expert's tasks as
@@ -562,8 +564,7 @@ constexpr int pair_smem() {
 template <int TTG, int P, bool kShared, int OCC = 2, int kLdsB = kPairLdsB, bool kSgRows = false,
           bool kFront = false>
 __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG, kLdsB>()];
-  static_assert(!kSgRows || pair_smem<TTG, kLdsB>() >= kSdSmem, "LDS of the shared task");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG, kLdsB, kSgRows ? kSgTokGu : 0>()];
   static_assert(pair_smem<TTG, kLdsB>() >= sizeof(BucketLds) + 4 * kMaxTokens * 8,
                 "LDS of the routing front");
   auto red = reinterpret_cast<f32x4_t(*)[kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave]>(smem);
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a)
     t -= a.front;
   }
   if constexpr (kShared) {
-    constexpr int GS = 16 * kSharedTTG;
+    constexpr int GS = kSgRows ? kSgTokGu : 16 * kSharedTTG;
     const int RBs = 2 * a.Is / kRowsPerBlock;
     const int n_sg = (a.S + GS - 1) / GS;
     if (t < n_sg * RBs) {
@@ -586,8 +587,8 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a)
       const int row0 = grp * GS, ntok = min(GS, a.S - row0);
       const uint8_t* tiles = a.ws13 + static_cast<size_t>(rb) * NC * kBfTileBytes;
       if constexpr (kSgRows) {
-        static_assert(GS == kSdTok, "token groups of the shared task");
-        shared_rows_task<MOE_SG_PW, true>(tiles, NC, a.x, a.d, row0, ntok, rb, a.hs, a.Is, smem);
+        shared_rows_task<MOE_SG_PW, true, kSgTokGu>(tiles, NC, a.x, a.d, row0, ntok, rb, a.hs, a.Is,
+                                                    smem);
       } else {
         ffn_task<false, kSharedTTG, kSharedP, true, false>(
             tiles, NC, a.x, a.d, row0, ntok, rb, a.hs, a.Is, [](int r) { return r; }, NoWait{},
@@ -637,18 +638,17 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void gate_up_kernel(FfnArgs a)
 // workgroups a CU; routed tasks with rows of at most kLdsB bytes stage them in
 // LDS; kSgRows: the shared tasks run as shared_rows_task.
 #ifndef MOE_SD_PW
-#define MOE_SD_PW 4  // weight chunks in flight a wave, shared down tasks
+#define MOE_SD_PW (MOE_SG_TOK_DN > 32 ? 2 : 4)  // weight chunks in flight a wave, shared down tasks
 #endif
 template <int TTG, int P, bool kShared, int OCC = 2, int kLdsB = kPairLdsB, bool kSgRows = false>
 __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG, kLdsB>()];
-  static_assert(!kSgRows || pair_smem<TTG, kLdsB>() >= kSdSmem, "LDS of the shared down task");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[pair_smem<TTG, kLdsB, kSgRows ? kSgTokDn : 0>()];
   auto red = reinterpret_cast<f32x4_t(*)[kSharedTTG > TTG ? kSharedTTG : TTG][4][kWave]>(smem);
   const int RB = a.d / kRowsPerBlock;
   auto same = [](int r) { return r; };
   int t = blockIdx.x;
   if constexpr (kShared) {
-    constexpr int GS = 16 * kSharedTTG;
+    constexpr int GS = kSgRows ? kSgTokDn : 16 * kSharedTTG;
     const int n_sg = (a.S + GS - 1) / GS;
     if (t < n_sg * RB) {
       const int NCs = a.Is / kChunkK;
@@ -658,8 +658,8 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
       const uint8_t* tiles = a.ws2 + static_cast<size_t>(rb) * NCs * kBfTileBytes;
       uint16_t* ys = a.y + static_cast<size_t>(a.R_max) * a.d;
       if constexpr (kSgRows) {
-        static_assert(GS == kSdTok, "token groups of the shared down task");
-        shared_rows_task<MOE_SD_PW, false>(tiles, NCs, a.hs, a.Is, row0, ntok, rb, ys, a.d, smem);
+        shared_rows_task<MOE_SD_PW, false, kSgTokDn>(tiles, NCs, a.hs, a.Is, row0, ntok, rb, ys,
+                                                     a.d, smem);
       } else {
         ffn_task<false, kSharedTTG, kSharedP, false, false>(
             tiles, NCs, a.hs, a.Is, row0, ntok, rb, ys, a.d, same, NoWait{},
@@ -699,10 +699,12 @@ __global__ __launch_bounds__(kSplit * kWave, OCC) void down_kernel(FfnArgs a) {
 // CU; a.front: the routing front ahead of the gate_up launch's tasks
 template <int TTG, int PG, int PD, bool kShared, bool kLean>
 void launch_pair(const FfnArgs& a, hipStream_t stream) {
-  constexpr int GS = 16 * kSharedTTG;
-  const int n_sg = kShared ? (a.S + GS - 1) / GS : 0;
-  const int g1 = a.front + n_sg * (2 * a.Is / kRowsPerBlock) + a.max_work * (2 * a.I / kRowsPerBlock);
-  const int g2 = (n_sg + a.max_work) * (a.d / kRowsPerBlock);
+  constexpr int GSG = kLean ? kSgTokGu : 16 * kSharedTTG;  // token groups of the shared tasks
+  constexpr int GSD = kLean ? kSgTokDn : 16 * kSharedTTG;
+  const int n_sgg = kShared ? (a.S + GSG - 1) / GSG : 0;
+  const int n_sgd = kShared ? (a.S + GSD - 1) / GSD : 0;
+  const int g1 = a.front + n_sgg * (2 * a.Is / kRowsPerBlock) + a.max_work * (2 * a.I / kRowsPerBlock);
+  const int g2 = (n_sgd + a.max_work) * (a.d / kRowsPerBlock);
   if (a.front) {
     if constexpr (kLean)
       hipLaunchKernelGGL((gate_up_kernel<TTG, PG, kShared, MOE_GU_OCC, MOE_GU_LDSB, true, true>),

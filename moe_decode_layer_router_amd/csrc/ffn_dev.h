@@ -538,31 +538,35 @@ __device__ __forceinline__ void ffn_task_ldsb(const uint8_t* __restrict__ tiles,
 }
 
 // ---------------------------------------------------------------------------
-// The shared expert for one 64-row block and one group of up to 32 tokens
+// The shared expert for one 64-row block and one group of up to TOK tokens
 // (Kimi-K3 layer page, "k2_launch": w_sgu and w_sd, the always-on expert's
 // gate_up and down), with waves owning row tiles instead of K quarters: wave w
 // streams row tile w over all NC chunks through a ring of PW chunks (16 VGPRs
-// a chunk) and needs no reduction across waves. The chunk's B rows (32 x 128
+// a chunk) and needs no reduction across waves. The chunk's B rows (TOK x 128
 // bf16: token rows of x for gate_up, SwiGLU rows for down) are staged in LDS
 // once for the 4 waves, two chunks ahead through registers, in two buffers
 // whose rows are padded to 272 bytes so that the 16 rows one ds_read_b128
-// touches fall on distinct banks. Workgroup-level; smem: kSdSmem bytes.
+// touches fall on distinct banks. Workgroup-level; smem: sd_smem<TOK>() bytes.
 // Output rows row0 .. row0 + ntok - 1 of out (row length out_ld): gate_up
 // rounds gate and up to bf16 and writes SwiGLU rows, down writes bf16 rows.
-constexpr int kSdTok = 32;
-constexpr int kSdPitch = 136;                  // bf16 a staged row (128 + 8 pad)
-constexpr int kSdBuf = kSdTok * kSdPitch;      // bf16 a buffer
-constexpr int kSdSmem = 2 * kSdBuf * 2;        // bytes
+constexpr int kSdPitch = 136;  // bf16 a staged row (128 + 8 pad)
+template <int TOK>
+constexpr int sd_buf() { return TOK * kSdPitch; }  // bf16 a buffer of TOK rows
+template <int TOK>
+constexpr int sd_smem() { return 2 * sd_buf<TOK>() * 2; }  // bytes (two buffers)
 
-template <int PW, bool kGateUp>
+// TOK: tokens of the group (32 or 64)
+template <int PW, bool kGateUp, int TOK>
 __device__ __forceinline__ void shared_rows_task(const uint8_t* __restrict__ tiles, int NC,
                                                  const uint16_t* __restrict__ bsrc, int K, int row0,
                                                  int ntok, int rb, uint16_t* __restrict__ out,
                                                  int out_ld, uint8_t* smem) {
   static_assert(PW % 2 == 0, "the stage registers alternate with the chunk's parity");
+  static_assert(TOK % 16 == 0 && TOK <= 64, "token tiles of 16");
   constexpr int kThreads = kSplit * kWave;
-  constexpr int kPer = kSdTok * 16 / kThreads;  // 16-byte pieces a thread stages a chunk
-  constexpr int NTT = kSdTok / 16;
+  constexpr int kSdBuf = sd_buf<TOK>();
+  constexpr int kPer = TOK * 16 / kThreads;  // 16-byte pieces a thread stages a chunk
+  constexpr int NTT = TOK / 16;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;

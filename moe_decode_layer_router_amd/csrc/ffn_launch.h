@@ -7,7 +7,20 @@
 
 namespace moeblk {
 
-constexpr int kSharedTTG = 2;  // shared expert: 32-token groups
+constexpr int kSharedTTG = 2;  // shared expert at S <= 16: 32-token groups
+// shared expert at S > 16 (shared_rows_task in both launches): tokens a
+// group in the gate_up launch and in the down launch. Measured at S = 128
+// (d = 7168, I_s = 2048), kernel us with 32 / 64 tokens: gate_up 101.7 /
+// 105.3, down 50.8 / 46.9 (the down tasks' weights, read once per group,
+// come through L2 half as often).
+#ifndef MOE_SG_TOK_GU
+#define MOE_SG_TOK_GU 32
+#endif
+#ifndef MOE_SG_TOK_DN
+#define MOE_SG_TOK_DN 64
+#endif
+constexpr int kSgTokGu = MOE_SG_TOK_GU;
+constexpr int kSgTokDn = MOE_SG_TOK_DN;
 #ifndef MOE_SHARED_P
 #define MOE_SHARED_P 2
 #endif
