@@ -29,13 +29,10 @@ constexpr int kRouteSplitMinS = 32;
 #define MOE_ROUTE_MAX_WG 256
 #endif
 constexpr int kMaxRouteParts = MOE_ROUTE_MAX_PARTS;  // K parts of the split router, at most
-// K a lane a block of the split router (block = 4 KL K): with 8 the lanes of
-// one K group read whole 128-byte lines of the router rows. Router us, 8 / 4:
-// S = 64 6.01 / 6.49, S = 96 8.53 / 10.03, S = 128 (d = 7168) 12.04 / 14.09.
-#ifndef MOE_ROUTE_KL
-#define MOE_ROUTE_KL 8
-#endif
-constexpr int kRouteKL = MOE_ROUTE_KL;
+// K a lane a block of the split router (block = 4 KL = 32 K): the 8 K of a
+// lane are one operand of the bf16 MFMA, and the lanes of one K group read
+// whole 128-byte lines of the router rows
+constexpr int kRouteKL = 8;
 constexpr int kRouteKB = 4 * kRouteKL;  // K a block
 inline int router_tile_tok(int S) { return S <= 64 ? 32 : 64; }
 inline int router_parts(const moe_dims& m) {

@@ -489,8 +489,14 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
 }
 
 // ---------------------------------------------------------------------------
-// Router logits for S > 32 as a tiled product split over K, on fp32 MFMA
-// (v_mfma_f32_16x16x4_f32: A = 16 router rows x 4 K, B = 4 K x 16 tokens).
+// Router logits for S > 32 as a tiled product split over K, on bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16: A = 16 router rows x 32 K, B = 32 K x 16 tokens).
+// The token rows are bf16 already; each fp32 router weight is split into three
+// bf16 (split_bf16x3) whose sum is the weight exactly, and the three products
+// with the bf16 token value are exact in fp32, so the three MFMAs a block add
+// every exact product x w in fp32: the logit keeps fp32 accuracy (an
+// accumulation order of its own) at 3 MFMAs of 16 cycles where the fp32
+// 16 x 16 x 4 MFMA took 8 of 32 cycles.
 //
 // A workgroup of 4 waves owns TT tokens x 64 router rows over one K part of
 // Kp: part p covers K [p Kp, (p + 1) Kp). It writes its tile unreduced to
@@ -500,18 +506,17 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits,
 // keeps every CU busy.
 //
 // Wave w takes tokens (w & 1) TT / 2 .. + TT / 2 and rows (w >> 1) 32 .. + 32:
-// NT = TT / 32 token tiles x 2 row tiles of 16 x 16. In a block of KB = 4 KL
-// K a lane loads KL consecutive K of one router row (4 KL bytes) and of one
-// token row (KL bf16); MFMA step s takes K index KL (lane / 16) + s of the
-// block in both operands, so every product of the block is summed once. With
-// KL = 8 the 16 lanes of one K group read whole 128-byte lines of 16 rows.
+// NT = TT / 32 token tiles x 2 row tiles of 16 x 16. In a block of KB = 32 K a
+// lane loads 8 consecutive K of one router row (32 bytes) and of one token row
+// (8 bf16), K 8 (lane / 16) .. + 7 of the block: the MFMA's operand layout in
+// both. The 16 lanes of one K group read whole 128-byte lines of 16 rows.
 // Block b accumulates
 // into set b % 4; the sets are added as (0 + 1) + (2 + 3), which keeps the
 // sequential chains a quarter of the part. Rows past E and tokens past S
 // repeat the last one and are not stored.
 constexpr int kRouteTileE = 64;
 #ifndef MOE_ROUTE_RING
-#define MOE_ROUTE_RING (32 / MOE_ROUTE_KL)
+#define MOE_ROUTE_RING 4
 #endif
 constexpr int kRouteRing = MOE_ROUTE_RING;  // blocks in flight a wave
 
@@ -531,34 +536,52 @@ __device__ __forceinline__ void route_blk_load(RouteBlk<NT>& b, const float* con
       b.w[i][v] = *reinterpret_cast<const f32x4_t*>(wrow[i] + kRouteKB * blk + 4 * v);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    if constexpr (kRouteKL == 8) {
-      const uint4 u = *reinterpret_cast<const uint4*>(xrow[j] + kRouteKB * blk);
-      b.x[j][0] = u.x; b.x[j][1] = u.y; b.x[j][2] = u.z; b.x[j][3] = u.w;
-    } else {
-      const uint2 u = *reinterpret_cast<const uint2*>(xrow[j] + kRouteKB * blk);
-      b.x[j][0] = u.x; b.x[j][1] = u.y;
-    }
+    const uint4 u = *reinterpret_cast<const uint4*>(xrow[j] + kRouteKB * blk);
+    b.x[j][0] = u.x; b.x[j][1] = u.y; b.x[j][2] = u.z; b.x[j][3] = u.w;
   }
+}
+
+// fp32 w as hi + mid + lo, three bf16 whose sum is w exactly: hi keeps the
+// top 8 significant bits (truncated), mid the top 8 of the remainder, lo the
+// rest (at most 8 bits); each subtraction is exact in fp32 (for |w| below
+// about 2^-110 the remainders are subnormal and lo may drop low bits)
+__device__ __forceinline__ void split_bf16x3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t wb = __float_as_uint(w);
+  const uint32_t hb = wb & 0xffff0000u;
+  const float r1 = w - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  hi = hb >> 16;
+  mid = mb >> 16;
+  lo = __float_as_uint(r2) >> 16;
 }
 
 template <int NT>
 __device__ __forceinline__ void route_blk_mfma(const RouteBlk<NT>& b, f32x4_t (&acc)[2][NT]) {
-  float xf[NT][kRouteKL];
+  static_assert(kRouteKL == 8, "a lane's 8 K are the bf16 MFMA's operand");
+  bf16x8_t xv[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j)
+    xv[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{b.x[j][0], b.x[j][1], b.x[j][2], b.x[j][3]});
 #pragma unroll
-    for (int h = 0; h < kRouteKL / 2; ++h) {
-      xf[j][2 * h] = bf16_lo(b.x[j][h]);
-      xf[j][2 * h + 1] = bf16_hi(b.x[j][h]);
+  for (int i = 0; i < 2; ++i) {
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) split_bf16x3(b.w[i][k / 4][k % 4], h[k], m[k], l[k]);
+    u32x4_t hv, mv, lv;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hv[q] = h[2 * q] | (h[2 * q + 1] << 16);
+      mv[q] = m[2 * q] | (m[2 * q + 1] << 16);
+      lv[q] = l[2 * q] | (l[2 * q + 1] << 16);
     }
 #pragma unroll
-  for (int st = 0; st < kRouteKL; ++st)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.w[i][st / 4][st % 4], xf[j][st],
-                                                           acc[i][j], 0, 0, 0);
+    for (int j = 0; j < NT; ++j) {
+      acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8_t, lv), xv[j], acc[i][j]);
+      acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8_t, mv), xv[j], acc[i][j]);
+      acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8_t, hv), xv[j], acc[i][j]);
+    }
+  }
 }
 
 // Workgroup (4 waves): tile (tt, et) of K part p.
