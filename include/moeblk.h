@@ -383,7 +383,8 @@ int moe_latent_norm(const moe_proj_dims* dims, const void* h_raw, const void* ga
  *   w_packed moe_pack_dense of w_post [N, K] bf16;
  *   out      [S, N] bf16, written: bf16(sum_k bf16(partial[t][k]) w_post[n][k]),
  *            fp32 accumulation as in moe_pre_expert.
- * Two launches: the rounding of the partial, then the projection. */
+ * One launch at S <= 16 (its tasks round the partial as they read it); above,
+ * two: the rounding of the partial, then the projection. */
 int moe_post_expert(const moe_proj_dims* dims, const float* partial, const void* w_packed,
                     void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 

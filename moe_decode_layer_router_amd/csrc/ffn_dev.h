@@ -143,6 +143,36 @@ struct BRows {
   }
 };
 
+// fp32 B rows (kF32In: the post-expert projection's summed partial), each
+// value rounded to bf16 where the chunk is used, as one rounding launch
+// before the GEMM would: the lane's K 32 g + 8 q .. + 7 as two float4s a step
+template <int TTG>
+struct BfChunkF32 {
+  u32x4_t w[4][4];
+  u32x4_t b[TTG][8];  // step q: floats 8 q .. 8 q + 3, then 8 q + 4 .. 8 q + 7
+};
+
+template <int TTG>
+struct BRowsF32 {
+  const float* bp[TTG];
+
+  // bsrc: the fp32 rows (K floats each), passed as the byte-compatible pointer
+  __device__ __forceinline__ void init(const uint16_t* bsrc, int K, const int (&src)[TTG], int g) {
+    const float* f = reinterpret_cast<const float*>(bsrc);
+#pragma unroll
+    for (int tt = 0; tt < TTG; ++tt) bp[tt] = f + static_cast<size_t>(src[tt]) * K + 32 * g;
+  }
+
+  __device__ __forceinline__ void load(u32x4_t (&b)[TTG][8], int c) const {
+#pragma unroll
+    for (int tt = 0; tt < TTG; ++tt) {
+      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(bp[tt] + c * kChunkK);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[tt][i] = p[i];
+    }
+  }
+};
+
 template <int TTG>
 __device__ __forceinline__ void load_w(MxChunk<TTG>& ch, const uint8_t* wlane, const uint8_t* slane,
                                        int c) {
@@ -155,15 +185,23 @@ __device__ __forceinline__ void load_w(MxChunk<TTG>& ch, const uint8_t* wlane, c
 // Dense bf16 tiles (the shared expert, the latent projections) are read once
 // per token group, by tasks placed on one XCD (group_task): plain loads, so
 // the groups after the first find them in that XCD's L2.
-template <int TTG>
-__device__ __forceinline__ void load_w(BfChunk<TTG>& ch, const uint8_t* wlane, const uint8_t*,
-                                       int c) {
+__device__ __forceinline__ void load_bf_w(u32x4_t (&w)[4][4], const uint8_t* wlane, int c) {
   const uint8_t* t = wlane + static_cast<size_t>(c) * kBfTileBytes;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      ch.w[r][q] = *reinterpret_cast<const u32x4_t*>(t + r * 4096 + q * 1024);
+      w[r][q] = *reinterpret_cast<const u32x4_t*>(t + r * 4096 + q * 1024);
+}
+template <int TTG>
+__device__ __forceinline__ void load_w(BfChunk<TTG>& ch, const uint8_t* wlane, const uint8_t*,
+                                       int c) {
+  load_bf_w(ch.w, wlane, c);
+}
+template <int TTG>
+__device__ __forceinline__ void load_w(BfChunkF32<TTG>& ch, const uint8_t* wlane, const uint8_t*,
+                                       int c) {
+  load_bf_w(ch.w, wlane, c);
 }
 
 // One MXFP4 chunk tile (kMxTileBytes: 4 row tiles of 64 lanes x 16 bytes, then
@@ -209,6 +247,27 @@ __device__ __forceinline__ void compute_chunk(const MxChunk<TTG>& ch, f32x4_t (&
           acc[tt][r] = mfma_bf16(av, __builtin_bit_cast(bf16x8_t, ch.b[tt][q]), acc[tt][r]);
     }
   }
+}
+
+template <int TTG>
+__device__ __forceinline__ void compute_chunk(const BfChunkF32<TTG>& ch, f32x4_t (&acc)[TTG][4],
+                                              int n_tt) {
+  // step q of every (token tile, row tile): each accumulator still takes the
+  // steps in order, as in the bf16 chunk
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int tt = 0; tt < TTG; ++tt) {
+      if (tt >= n_tt) continue;
+      const f32x4_t l = __builtin_bit_cast(f32x4_t, ch.b[tt][2 * q]);
+      const f32x4_t h = __builtin_bit_cast(f32x4_t, ch.b[tt][2 * q + 1]);
+      const u32x4_t bq{pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]), pack_bf16x2(h[0], h[1]),
+                       pack_bf16x2(h[2], h[3])};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[tt][r] = mfma_bf16(__builtin_bit_cast(bf16x8_t, ch.w[r][q]),
+                               __builtin_bit_cast(bf16x8_t, bq), acc[tt][r]);
+    }
 }
 
 template <int TTG>
@@ -302,8 +361,10 @@ struct NoWait {
 // of the single launch) then has P + PL chunks in flight at the register cost
 // of P. The LDS is read only after every vector load of the wave has arrived.
 // kOutCoh (down): the output rows go through to the coherence point.
+// kF32In (dense): bsrc holds fp32 rows (K floats each), rounded to bf16 as
+// they are used.
 template <bool kMx, int TTG, int P, bool kGateUp, bool kCoh, bool kF32Out = false, int PL = 0,
-          bool kOutCoh = false, class SrcOf, class BeforeB>
+          bool kOutCoh = false, bool kF32In = false, class SrcOf, class BeforeB>
 __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int NC,
                                          const uint16_t* __restrict__ bsrc, int K, int row0,
                                          int ntok, int rb, uint16_t* __restrict__ out, int out_ld,
@@ -324,8 +385,11 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
 #pragma unroll
   for (int tt = 0; tt < TTG; ++tt) src[tt] = src_of(row0 + min(tt * 16 + col, ntok - 1));
 
-  using Chunk = typename std::conditional<kMx, MxChunk<TTG>, BfChunk<TTG>>::type;
+  using Chunk = typename std::conditional<
+      kMx, MxChunk<TTG>,
+      typename std::conditional<kF32In, BfChunkF32<TTG>, BfChunk<TTG>>::type>::type;
   static_assert(PL == 0 || kMx, "LDS-staged chunks are MXFP4 tiles");
+  static_assert(!kF32In || (!kMx && !kCoh), "fp32 B rows: dense tiles, plain loads");
   const int my_n = (NC - w + kSplit - 1) / kSplit;  // this wave's chunks: w, w + 4, ...
   Chunk ring[P];
 #pragma unroll
@@ -350,7 +414,7 @@ __device__ __forceinline__ void ffn_task(const uint8_t* __restrict__ tiles, int 
 
   before_b();
 
-  BRows<TTG, kCoh && !kGateUp> bp;
+  typename std::conditional<kF32In, BRowsF32<TTG>, BRows<TTG, kCoh && !kGateUp>>::type bp;
   bp.init(bsrc, K, src, g);
 #pragma unroll
   for (int i = 0; i < P; ++i) bp.load(ring[i].b, min(w + kSplit * i, NC - 1));

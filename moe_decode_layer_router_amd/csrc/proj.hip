@@ -18,8 +18,9 @@
 // groups of one (row block, K part) run on one XCD and share its L2 for the
 // weights (group_task). In moe_pre_expert the router rows on the same input
 // are extra workgroups of the same launch (the K5 page's "router and
-// pre_expert_proj" on ffn_in). The post step first rounds its fp32 input to
-// bf16 (one small launch).
+// pre_expert_proj" on ffn_in). The post step's 16-token tasks (S <= 16) read
+// its fp32 input directly and round each value to bf16 where they use it;
+// above, one small launch rounds the input first.
 #include "combine_dev.h"
 #include "ffn_dev.h"
 #include "host.h"
@@ -56,7 +57,7 @@ inline int proj_parts(const moe_proj_dims& m) {
 }
 
 // workspace: fp32 partials [KP][S][N], the counters [N / 64][token groups]
-// (zero between calls), the post step's bf16 input [S][K]
+// (zero between calls), then at S > 16 the post step's bf16 input [S][K]
 struct ProjLayout {
   size_t part, ctr, in16, total;
   int kp;
@@ -69,13 +70,14 @@ ProjLayout proj_layout(const moe_proj_dims& m) {
   l.part = 0;
   l.ctr = round_up(static_cast<size_t>(l.kp) * m.S * m.N * 4, 256);
   l.in16 = l.ctr + round_up(static_cast<size_t>(m.N / kRowsPerBlock) * ((m.S + G - 1) / G) * 4, 256);
-  l.total = l.in16 + round_up(static_cast<size_t>(m.S) * m.K * 2, 256);
+  l.total = l.in16 + (proj_ttg(m) > 1 ? round_up(static_cast<size_t>(m.S) * m.K * 2, 256) : 0);
   return l;
 }
 
 struct ProjArgs {
   const uint8_t* w;   // packed dense weight [N][K]
-  const uint16_t* in; // [S][K] bf16
+  const uint16_t* in; // [S][K] bf16, or NULL with in32
+  const float* in32;  // [S][K] fp32 (rounded to bf16 as the tasks use it), or NULL
   float* part;        // workspace: fp32 partials
   int32_t* ctr;       // workspace: parts done a (row block, token group)
   uint16_t* out;      // [S][N] bf16
@@ -97,8 +99,9 @@ constexpr int kRouterTok = 16;  // tokens a router workgroup
 // task that completes the count sums the KP partials in part order with
 // coherent loads, rounds to bf16, writes the output and resets the count. No
 // workgroup waits for another.
-template <int TTG, int RNW>
+template <int TTG, int RNW, bool kF32In = false>
 __global__ __launch_bounds__(kSplit * kWave, 2) void proj_kernel(ProjArgs a) {
+  static_assert(!kF32In || RNW == 0, "router rows read bf16 rows");
   __shared__ f32x4_t red[kSplit][TTG][4][kWave];
   __shared__ int last;
   int t = blockIdx.x;
@@ -126,9 +129,13 @@ __global__ __launch_bounds__(kSplit * kWave, 2) void proj_kernel(ProjArgs a) {
   const uint8_t* tiles =
       a.w + (static_cast<size_t>(rb) * NC + static_cast<size_t>(kp) * NCp) * kBfTileBytes;
   const size_t SN = static_cast<size_t>(a.S) * a.N;
-  ffn_task<false, TTG, kProjP, false, false, true>(
-      tiles, NCp, a.in + static_cast<size_t>(kp) * NCp * kChunkK, a.K, row0, ntok, rb,
-      reinterpret_cast<uint16_t*>(a.part + kp * SN), a.N, [](int r) { return r; }, NoWait{}, red);
+  const size_t k0 = static_cast<size_t>(kp) * NCp * kChunkK;
+  const uint16_t* bsrc =
+      kF32In ? reinterpret_cast<const uint16_t*>(a.in32 + k0) : a.in + k0;
+  static_assert(!kF32In || TTG == 1, "fp32 rows: 16-token tasks");
+  ffn_task<false, TTG, kProjP, false, false, true, 0, false, kF32In>(
+      tiles, NCp, bsrc, a.K, row0, ntok, rb, reinterpret_cast<uint16_t*>(a.part + kp * SN), a.N,
+      [](int r) { return r; }, NoWait{}, red);
 
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's partial stores are done
   __syncthreads();
@@ -217,7 +224,9 @@ __global__ __launch_bounds__(kNormThreads) void latent_norm_kernel(const uint16_
   }
 }
 
-// the fp32 partial handed to the bf16 GEMM: round to bf16, 4 values a thread
+// the fp32 partial handed to the bf16 GEMM at S > 16: rounded to bf16 by a
+// launch of its own, 4 values a thread (32-token tasks have no registers
+// left for fp32 rows)
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ in,
                                                       uint16_t* __restrict__ out, int n) {
   const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -233,6 +242,12 @@ void launch_proj_t(const ProjArgs& a, int grid, hipStream_t stream) {
 
 template <int TTG>
 void launch_proj_r(const ProjArgs& a, int grid, hipStream_t stream) {
+  if constexpr (TTG == 1) {
+    if (a.in32) {
+      hipLaunchKernelGGL((proj_kernel<1, 0, true>), dim3(grid), dim3(kSplit * kWave), 0, stream, a);
+      return;
+    }
+  }
   if (a.E == 0) return launch_proj_t<TTG, 0>(a, grid, stream);
   switch (proj_router_nw(a.K)) {
     case 1: return launch_proj_t<TTG, 1>(a, grid, stream);
@@ -242,16 +257,18 @@ void launch_proj_r(const ProjArgs& a, int grid, hipStream_t stream) {
   }
 }
 
-// The projection of in [S][K] bf16 through packed w into out [S][N] bf16,
-// with E router rows of the same input in the same launch (E = 0: none)
+// The projection of in [S][K] bf16 (or in32 [S][K] fp32, each value rounded
+// to bf16) through packed w into out [S][N] bf16, with E router rows of the
+// same bf16 input in the same launch (E = 0: none)
 void launch_proj(const moe_proj_dims& m, const uint16_t* in, const void* w_packed,
                  uint16_t* out, const float* wr, const float* bias, float* logits, int E,
-                 void* workspace, hipStream_t stream) {
+                 void* workspace, hipStream_t stream, const float* in32 = nullptr) {
   const ProjLayout l = proj_layout(m);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   ProjArgs a{};
   a.w = static_cast<const uint8_t*>(w_packed);
   a.in = in;
+  a.in32 = in32;
   a.part = reinterpret_cast<float*>(ws + l.part);
   a.ctr = reinterpret_cast<int32_t*>(ws + l.ctr);
   a.out = out;
@@ -347,11 +364,18 @@ extern "C" int moe_post_expert(const moe_proj_dims* dims, const float* partial, 
   MOE_REQUIRE(aligned16(partial) && aligned16(w_packed) && aligned16(out) && aligned16(workspace),
               MOE_ERR_ALIGN);
   MOE_REQUIRE(workspace_bytes >= moe_proj_workspace_bytes(dims), MOE_ERR_WORKSPACE);
-  uint16_t* in16 = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + proj_layout(m).in16);
-  const int n = m.S * m.K;
-  hipLaunchKernelGGL(to_bf16_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, stream, partial, in16, n);
-  launch_proj(m, in16, w_packed, static_cast<uint16_t*>(out), nullptr, nullptr, nullptr, 0, workspace,
-              stream);
+  if (proj_ttg(m) == 1) {  // 16-token tasks round the fp32 rows as they use them
+    launch_proj(m, nullptr, w_packed, static_cast<uint16_t*>(out), nullptr, nullptr, nullptr, 0,
+                workspace, stream, partial);
+  } else {
+    uint16_t* in16 =
+        reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + proj_layout(m).in16);
+    const int n = m.S * m.K;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, stream, partial,
+                       in16, n);
+    launch_proj(m, in16, w_packed, static_cast<uint16_t*>(out), nullptr, nullptr, nullptr, 0,
+                workspace, stream);
+  }
   return launch_status();
 }
 
