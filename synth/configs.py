@@ -40,6 +40,9 @@ class MoeConfig:
     zipf_s: float = 0.0  # "zipf" exponent
     x_std: float = 1.0
     wr_std: float = 0.02
+    # router weights: "normal" N(0, wr_std); "wide": sign x U[1, 2) x 2^U[-40, 4),
+    # with about 5% exact zeros (magnitudes over 44 binades)
+    wr_kind: str = "normal"
     ws_std: float = 0.02  # shared-expert weights
     e8m0_lo: int = 119  # e8m0 scale bytes drawn uniformly from [lo, hi]
     e8m0_hi: int = 127

@@ -8,7 +8,7 @@ stream. Layouts are the canonical row-major ones the C ABI documents:
 key        shape                                 dtype
 =========  ====================================  =======
 x          [S, d]                                bf16 bits (uint16)
-wr         [E, d]                                float32
+wr         [E, d]                                float32 (wr_kind)
 bias       [E] or None                           float32
 w13q       [n_local, 2 I, d / 2]  (2 e2m1/byte)  uint8
 w13s       [n_local, 2 I, d / 32] (e8m0)         uint8
@@ -117,9 +117,16 @@ def make_inputs(
             _rng(seed, "x").standard_normal((S, d), dtype=np.float32) * cfg.x_std
         )
     if need("wr"):
-        out["wr"] = (
-            _rng(seed, "wr").standard_normal((E, d), dtype=np.float32) * cfg.wr_std
-        ).astype(np.float32)
+        if cfg.wr_kind == "wide":
+            r = _rng(seed, "wr")
+            mag = r.uniform(1.0, 2.0, (E, d)) * np.exp2(r.uniform(-40.0, 4.0, (E, d)))
+            sign = np.where(r.random((E, d)) < 0.5, -1.0, 1.0)
+            keep = r.random((E, d)) >= 0.05
+            out["wr"] = (sign * mag * keep).astype(np.float32)
+        else:
+            out["wr"] = (
+                _rng(seed, "wr").standard_normal((E, d), dtype=np.float32) * cfg.wr_std
+            ).astype(np.float32)
     if need("bias"):
         out["bias"] = router_bias(cfg)
     if need("w13q"):

@@ -68,15 +68,17 @@ def logit_roundings(cfg, dims) -> float:
     summation order moe_route documents (the pages fix fp32 accumulation, not
     an order). Without scratch (S <= 32): a thread sums d / 1024 products (d / 256 roundings
     counting each product and each add, generously), then a tree of 12 levels
-    (64 lanes, 16 waves) and the bias. With scratch: in a K part of Kp, each of 4
-    chains takes Kp / 16 MFMA steps of 4 products (at most 5 roundings a
-    step), the chains are added pairwise (2), each of 4 waves adds P / 4
+    (64 lanes, 16 waves) and the bias. With scratch: every product of a bf16
+    token value with one of the three bf16 pieces of a weight is exact in fp32;
+    in a K part of Kp, each of 4 chains takes ceil(Kp / 128) blocks of 3 MFMAs,
+    each adding 32 products to its accumulator (at most 32 roundings, counting
+    every add), the chains are added pairwise (2), each of 4 waves adds P / 4
     parts, the waves pairwise (2), then the bias (1); P from the scratch size
     moe_route asks for."""
     P = mb.moe_route_workspace_bytes(dims) // (cfg.S * cfg.E * 4)
     if P == 0:
         return cfg.d / 256 + 12
-    return 5 * (cfg.d / P) / 16 + 2 + P / 4 + 2 + 1
+    return 3 * 32 * -(-(cfg.d // P) // 128) + 2 + P / 4 + 2 + 1
 
 
 def check_logits(inp, g) -> np.ndarray:

@@ -104,6 +104,17 @@ EDGE = {
 }
 
 
+@pytest.mark.parametrize("S", [33, 64, 128])
+def test_split_router_wide_weights(S):
+    """The split router (S > 32) splits each fp32 weight into three bf16 for
+    the bf16 MFMA; router weights spread over 44 binades, both signs and exact
+    zeros, hold its logits to the same fp32 bound and its top-k to the
+    oracle's (check_block)."""
+    cfg = _tiny(S=S, d=1024, E=64, n_local=8, local_base=8, topk=4, wr_kind="wide")
+    inp = make_inputs(cfg, 21, gamma="random")
+    check_block(inp, run_gpu(inp))
+
+
 @pytest.mark.parametrize("name", list(EDGE))
 def test_edge_cases(name):
     inp = make_inputs(EDGE[name], 11, gamma="random")
