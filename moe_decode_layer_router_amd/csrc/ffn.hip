@@ -173,20 +173,44 @@ __device__ __forceinline__ void route_front(const FfnArgs& a, int b, uint8_t* sm
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores and atomics are done
     __syncthreads();
-    if (threadIdx.x < kDoneCopies)
+    if (a.S > kTopkLinesMinS) {
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(&f.tkc[(b % kTopkLines) * kCtlStride], 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if (threadIdx.x < kDoneCopies) {
       __hip_atomic_fetch_add(&f.done[threadIdx.x * kCtlStride], 1, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
+    }
     return;
   }
-  if (threadIdx.x == 0) {
+  if (a.S <= kTopkLinesMinS) {
+    if (threadIdx.x == 0) {
+      const long long t0 = clock64();
+      while (__hip_atomic_load(f.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.S) {
+        __builtin_amdgcn_s_sleep(4);
+        if (clock64() - t0 > kWaitCycles) {
+          __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+  } else if (threadIdx.x < kWave) {
+    // lane l < kTopkLines watches line l until it holds its count of top-k
+    // workgroups (bounded), then the counter's copies are set to S
+    const int lane = threadIdx.x;
+    const int l = min(lane, kTopkLines - 1);
+    const int need = (a.S - l + kTopkLines - 1) / kTopkLines;
     const long long t0 = clock64();
-    while (__hip_atomic_load(f.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.S) {
+    while (!__all(__hip_atomic_load(&f.tkc[l * kCtlStride], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) >= need)) {
       __builtin_amdgcn_s_sleep(4);
       if (clock64() - t0 > kWaitCycles) {
-        __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
+    if (lane < kDoneCopies)
+      __hip_atomic_store(&f.done[lane * kCtlStride], a.S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if constexpr (kOne) count_seen(a);
   BucketLds& L = *reinterpret_cast<BucketLds*>(smem);
@@ -795,6 +819,7 @@ int launch_ffn(const moe_dims& m, const void* x, const void* w13, const void* w2
     f.rdone = blk + kFrontRouterWord;
     f.seen = blk + kFrontSeenWord;
     f.cdone = blk + kFrontCombWord;
+    f.tkc = blk + kFrontTopkWord;
     f.E = m.E;
     f.topk = m.topk;
     f.renorm = m.renorm;

@@ -31,13 +31,19 @@ constexpr int kSharedP = MOE_SHARED_P;
 // launch's first workgroups (K3 page, stage "route": the routing is computed
 // inside the persistent launch that consumes it). A top-k workgroup sets its
 // token's bit in the token mask of each local expert it picked and counts
-// itself; the expert tasks wait for the count to reach S and take their
-// expert counts and bucket rows from the masks (a bucket row's token is the
-// rank-th set bit of its expert's mask, as the bucketing numbers them), so
-// the bucketing, which writes the ABI's bucket outputs, is not on their path.
-// The counter (kDoneCopies copies, one 128-byte line each) and the masks are
-// zero when the launch starts: a call leaves them at zero for the next one
-// (moe_forward's combine launch clears them).
+// itself on the counter (kDoneCopies copies, one 128-byte line each, which
+// spreads the tasks' polls). At S > kTopkLinesMinS it counts on line t mod
+// kTopkLines instead (device-scope atomics on one address serialise: S adds
+// on each copy cost about 13 ns each), and the bucketing workgroup waits for
+// the lines to add up to S, then sets the copies to S (s128_shared steps,
+// two boxes, two runs each: 162.5, 162.4 -> 159.8, 160.0 us and 161.6,
+// 163.9 -> 161.0, 161.0 us). The expert tasks wait for the
+// counter to reach S and take their expert counts and bucket rows from the
+// masks (a bucket row's token is the rank-th set bit of its expert's mask, as
+// the bucketing numbers them), so the bucketing, which writes the ABI's
+// bucket outputs, is not on their path. The lines, the counter and the masks
+// are zero when the launch starts: a call leaves them at zero for the next
+// one (moe_forward's combine launch clears them).
 //
 // The whole block as one launch (moe_forward_one_launch: no shared expert,
 // S <= 16, d <= 4096; K3 page, module docstring: the layer as one persistent
@@ -54,13 +60,17 @@ constexpr int kDoneCopies = 8;
 constexpr int kMaskWordsAll = 32 * 4;  // 32 local experts x 128 tokens
 constexpr int kRouterLines = 32;
 constexpr int kSeenLines = 64;
+constexpr int kTopkLines = 32;
+constexpr int kTopkLinesMinS = 32;
 // words of the front's control block: the counter copies, the masks, then
-// (one launch) the router rows' lines, the seen lines and the combine count
+// (one launch) the router rows' lines, the seen lines and the combine count,
+// then the top-k workgroups' lines
 constexpr int kFrontMaskWord = kDoneCopies * 32;
 constexpr int kFrontRouterWord = kFrontMaskWord + kMaskWordsAll;
 constexpr int kFrontSeenWord = kFrontRouterWord + kRouterLines * 32;
 constexpr int kFrontCombWord = kFrontSeenWord + kSeenLines * 32;
-constexpr int kFrontWords = kFrontCombWord + 32;
+constexpr int kFrontTopkWord = kFrontCombWord + 32;
+constexpr int kFrontWords = kFrontTopkWord + kTopkLines * 32;
 struct RouteFront {
   const float* logits_in;  // no K parts: the router's logits
   const float* parts;      // else the router's K parts [KP][S][E]
@@ -79,6 +89,7 @@ struct RouteFront {
   int32_t* pick_pos;
   int32_t* active;
   int32_t* done;           // workspace: kDoneCopies counters of finished top-k workgroups
+  int32_t* tkc;            // workspace: kTopkLines lines the top-k workgroups count on
   uint32_t* masks;         // workspace: [32][4] token masks of the local experts
   int E, topk, renorm, local_base;
 };
