@@ -153,8 +153,10 @@ size_t moe_route_workspace_bytes(const moe_dims* dims);
  *            calls sharing it must not overlap.
  * The fp32 sums run in a fixed order (deterministic): for S <= 32 each of
  * 1024 threads sums d / 1024 products and a fixed tree adds the threads'
- * sums; beyond, 32-K blocks of MFMA products go round-robin to 4 chains a
- * K part, added pairwise, and the parts are added in a fixed order. */
+ * sums; beyond, each weight is split exactly into three bf16 (whose products
+ * with the bf16 x are exact in fp32) and 32-K blocks of bf16 MFMAs go
+ * round-robin to 4 chains a K part, added pairwise, and the parts are added
+ * in a fixed order. */
 int moe_route(const moe_dims* dims, const void* x, const float* w_router, const float* bias,
               float* logits, int32_t* topk_ids, float* topk_w, void* workspace,
               size_t workspace_bytes, hipStream_t stream);
