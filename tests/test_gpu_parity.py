@@ -217,6 +217,30 @@ def test_more_row_counts(S):
         assert np.array_equal(g1[k], g[k]), k
 
 
+MAX_SIZES = {
+    # both intermediate sizes at their limit, S > 32 (split router, 32-row items, the
+    # shared expert's 64-token down groups)
+    "I8192_shared8192_S33": _tiny(S=33, d=1024, E=64, n_local=8, topk=4, I=8192, shared_I=8192),
+    # d at its limit with the shared expert at S > 32 (the combine's register path with
+    # the shared row)
+    "d16384_shared_S33": _tiny(S=33, d=16384, E=64, n_local=8, topk=4, I=128, shared_I=256),
+    # S, d and E at their limits (split router over d = 16384, 128 tokens)
+    "S128_d16384_E256": _tiny(S=128, d=16384, E=256, n_local=8, local_base=64, topk=8, I=128),
+}
+
+
+@pytest.mark.parametrize("name", list(MAX_SIZES))
+def test_max_sizes(name):
+    """The largest sizes moe_check_dims accepts, through the four calls against
+    the oracle (every token) and through moe_forward bit for bit."""
+    inp = make_inputs(MAX_SIZES[name], 31, gamma="random")
+    g = run_gpu(inp)
+    check_block(inp, g)
+    g1 = run_gpu(inp, g["blk"], fused=True)
+    for k in ("logits", "ids", "w", "counts", "offsets", "rows", "pick_pos", "active", "out"):
+        assert np.array_equal(g1[k], g[k]), k
+
+
 # ------------------------------------------------------------ moe_forward
 
 FUSED = {
