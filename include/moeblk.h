@@ -138,7 +138,8 @@ size_t moe_route_workspace_bytes(const moe_dims* dims);
 
 /* Router logits and top-k (K3 page stages "A" and "route"; K5 page, HA).
  *   x        [S, d] bf16 activations;
- *   w_router [E, d] fp32; bias [E] fp32 or NULL (bias_mode 0: added to the
+ *   w_router [E, d] fp32, finite (at S > 32 a non-finite weight makes its
+ *            expert's logits NaN); bias [E] fp32 or NULL (bias_mode 0: added to the
  *            logit, before ranking and sigmoid; 1: added to the ranking key
  *            only);
  *   logits   [S, E] fp32, written: sum_j x[t][j] w_router[e][j], fp32
